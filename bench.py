@@ -1,0 +1,231 @@
+"""Throughput of the FP8 block-scaled hot path on one MI355X.
+
+One step = online 1x128 quantization of the activations X [4096, 7168] (bf16),
+128x128 quantization of the weight W [2048, 7168] (bf16), and the block-scaled
+FP8 GEMM Y = X W^T [4096, 2048] with FP32 promotion per 128-deep K block
+(bf16 output by default).  Inputs are seeded synthetic tensors shaped like a
+DeepSeek-V3 layer (hidden 7168), already resident in HBM; W steps through
+several copies and X/Y through several buffers so that more than 1 GiB is
+cycled and the 256 MB Infinity Cache cannot serve repeated reads.
+
+Prints one JSON line.  `value` is whole-step throughput in TFLOP/s
+(2*M*N*K per step over the measured step time, quantization included); the
+`roofline` object covers the dominant kernel (the GEMM) with its average
+launch duration from HIP events recorded on the stream the kernels run on;
+`kernels` gives the same for each kernel, the quantizers as GB/s against HBM;
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, N, K = 4096, 2048, 7168
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
+
+# HBM bytes per GEMM launch from rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE, scaled
+# by the counters' reading for a copy kernel of known size; valid only for the
+# GEMM source it was measured on (sha256 of gemm.hip).
+TRAFFIC = {"gemm_sha256": None, "bytes_per_launch": None}
+
+
+def algorithmic():
+    tiles_x = M * (K // 128)
+    quant_x_bytes = M * K * 2 + M * K + tiles_x * 4
+    quant_w_bytes = N * K * 2 + N * K + (N // 128) * (K // 128) * 4
+    gemm_flops = 2 * M * N * K
+    return quant_x_bytes, quant_w_bytes, gemm_flops
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--out", choices=["bf16", "f32"], default="bf16")
+    p.add_argument("--rotate-mib", type=int, default=1100,
+                   help="bytes of input/output buffers cycled through (defeats the MALL)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=1024,
+                   help="rows of X in the oracle's timed sample")
+    return p.parse_args()
+
+
+def cpu_baseline(xbits, wbits, rows):
+    """The oracle, as it stands, on the first `rows` rows of X and all of W."""
+    import numpy as np
+    import oracle
+    from fp8_block_scaled_05_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        blas_threads = 1
+    x = synth.bf16_bits_to_f32(xbits[:rows])
+    w = synth.bf16_bits_to_f32(wbits)
+    t0 = time.perf_counter()
+    a, sa = oracle.quant_1x128(x)
+    b, sb = oracle.quant_128x128(w)
+    y, _ = oracle.blockscaled_gemm_ref(a, sa, b, sb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * N * K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "sample": (f"quantize X[:{rows}] (1x128) + W[{N},{K}] (128x128) + float64 "
+                       f"per-128-K-block GEMM with its error bound for {rows} rows; "
+                       f"{dt:.2f} s wall; quantizer single-threaded numpy, GEMM on "
+                       f"{blas_threads} BLAS threads"),
+            "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the quantize + GEMM path needs no collective; see the design notes).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    import fp8_block_scaled_05_amd as fb
+    from fp8_block_scaled_05_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    L = fb.lib()
+
+    print(f"[bench] generating linear workload X[{M},{K}] W[{N},{K}]", file=sys.stderr, flush=True)
+    inp = synth.workload_inputs(2)
+    xbits, wbits = inp["X"], inp["W"]
+    x0 = torch.from_numpy(xbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(wbits.view(np.int16)).view(torch.bfloat16).to(dev)
+    out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
+    set_bytes = x0.numel() * 2 + w0.numel() * 2 + M * N * (2 if args.out == "bf16" else 4)
+    n_sets = max(1, -(-args.rotate_mib * (1 << 20) // set_bytes))
+    xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
+    ws = [w0] + [w0.clone() for _ in range(n_sets - 1)]
+    ys = [torch.empty((M, N), dtype=out_dtype, device=dev) for _ in range(n_sets)]
+    a = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sa = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    b = torch.empty((N, K), dtype=torch.uint8, device=dev)
+    sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
+
+    stream = torch.cuda.current_stream()
+    hs = ctypes.c_void_p(stream.cuda_stream)
+    vp = ctypes.c_void_p
+    ycode = 0 if args.out == "bf16" else 1
+
+    def step(i):
+        """Three library calls on `stream`, with prepared arguments (no per-call checks)."""
+        j = i % n_sets
+        st = L.fp8_quant_act_1x128(vp(xs[j].data_ptr()), 0, M, K, K, 0, vp(a.data_ptr()), K,
+                                   vp(sa.data_ptr()), hs)
+        st |= L.fp8_quant_w_128x128(vp(ws[j].data_ptr()), 0, N, K, K, vp(b.data_ptr()), K,
+                                    vp(sb.data_ptr()), None, 0, None, hs)
+        st |= L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
+                                     vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
+                                     vp(ys[j].data_ptr()), ycode, N, hs)
+        if st:
+            raise RuntimeError(fb.last_error())
+
+    step(0)
+    torch.cuda.synchronize()
+
+    print(f"[bench] warmup {args.warmup} steps, {n_sets} buffer sets "
+          f"({n_sets * set_bytes / 2**20:.0f} MiB cycled)", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps, events around each kernel on the launch stream.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        j = i % n_sets
+        e = ev[i]
+        e[0].record(stream)
+        if L.fp8_quant_act_1x128(vp(xs[j].data_ptr()), 0, M, K, K, 0, vp(a.data_ptr()), K,
+                                 vp(sa.data_ptr()), hs):
+            raise RuntimeError(fb.last_error())
+        e[1].record(stream)
+        if L.fp8_quant_w_128x128(vp(ws[j].data_ptr()), 0, N, K, K, vp(b.data_ptr()), K,
+                                 vp(sb.data_ptr()), None, 0, None, hs):
+            raise RuntimeError(fb.last_error())
+        e[2].record(stream)
+        if L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
+                                  vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
+                                  vp(ys[j].data_ptr()), ycode, N, hs):
+            raise RuntimeError(fb.last_error())
+        e[3].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev])
+    avg_ms = per.mean(axis=0)
+    med_ms = np.median(per, axis=0)
+    qx_bytes, qw_bytes, flops = algorithmic()
+    gemm_tflops = flops / (avg_ms[2] * 1e-3) / 1e12
+    qx_gbps = qx_bytes / (avg_ms[0] * 1e-3) / 1e9
+    qw_gbps = qw_bytes / (avg_ms[1] * 1e-3) / 1e9
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    gemm_src = os.path.join(ROOT, "fp8_block_scaled_05_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(gemm_src, "rb").read()).hexdigest()
+    traffic = TRAFFIC["bytes_per_launch"] if TRAFFIC["gemm_sha256"] == sha else None
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": "linear layer: quantize X[4096,7168] 1x128 + W[2048,7168] "
+                               "128x128, GEMM Y[4096,2048] with FP32 promotion per 128-K block",
+                   "M": M, "N": N, "K": K, "out": args.out, "accumulate": "f32",
+                   "buffer_sets": n_sets},
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+                     "traffic": traffic},
+        "kernels": {
+            "quant_act_1x128": {"avg_us": round(avg_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2),
+                                "GB/s": round(qx_gbps, 1), "frac_hbm": round(qx_gbps / PEAK_HBM_GBPS, 4),
+                                "bytes": qx_bytes},
+            "quant_w_128x128": {"avg_us": round(avg_ms[1] * 1e3, 2), "median_us": round(med_ms[1] * 1e3, 2),
+                                "GB/s": round(qw_gbps, 1), "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4),
+                                "bytes": qw_bytes},
+            "blockscaled_gemm": {"avg_us": round(avg_ms[2] * 1e3, 2), "median_us": round(med_ms[2] * 1e3, 2),
+                                 "TFLOP/s": round(gemm_tflops, 2),
+                                 "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "flops": flops},
+        },
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the CPU oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(xbits, wbits, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

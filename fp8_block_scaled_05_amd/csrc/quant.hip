@@ -1,0 +1,404 @@
+// Online fine-grained E4M3 quantization kernels for gfx950.
+//
+// Method: codingmall.com knowledge-base article on FP8 precision in
+// DeepSeek-V3 training, sections "Finkornig kvantisering" (1x128 activation
+// tiles, 128x128 weight blocks, each with its own scale) and
+// "Online-kvantisering" (the scale comes from the tile's current values);
+// HolySheep AI (zh) FP8 mixed-precision article, section 2.2
+// (FP8BlockQuantizer.quantize: scale = amax/448, guarded to 1 when not above
+// 1e-10; codes = E4M3 of x/scale; the FP32 scale is returned).
+//
+// All three kernels are HBM-bound streaming kernels: every input byte is read
+// once with 16-byte loads, every code written once with 8- or 16-byte
+// stores.  Each 128-element tile's amax is reduced across the lanes that hold
+// it (a 16-lane DPP row for 1x128), the scale and its reciprocal are formed
+// once per tile, and x/s is evaluated with a 3-instruction exact quotient for
+// bf16 inputs (IEEE division for f32 inputs).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "device.hpp"
+#include "fp8bs.h"
+#include "status.hpp"
+
+namespace fp8bs {
+namespace {
+
+// ---------------------------------------------------------------------------
+// 8 consecutive input elements starting at p (16-byte aligned) as floats.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool kBf16>
+__device__ __forceinline__ void load8(const void* p, float (&v)[8]) {
+  if constexpr (kBf16) {
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x);
+    v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
+    v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z);
+    v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
+  } else {
+    const f32x4* f = reinterpret_cast<const f32x4*>(p);
+    const f32x4 a = __builtin_nontemporal_load(f);
+    const f32x4 b = __builtin_nontemporal_load(f + 1);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+template <bool kBf16>
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+  if constexpr (kBf16) return div_bf16_by_scale(x, s, r);
+  else return x / s;
+}
+
+template <bool kBf16>
+__device__ __forceinline__ uint2 encode8(const float (&v)[8], float s, float r) {
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = quotient<kBf16>(v[i], s, r);
+  return make_uint2(pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7]));
+}
+
+__device__ __forceinline__ float absmax8(const float (&v)[8]) {
+  float m0 = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fabsf(v[2]));
+  float m1 = fmaxf(fmaxf(fabsf(v[3]), fabsf(v[4])), fabsf(v[5]));
+  float m2 = fmaxf(fabsf(v[6]), fabsf(v[7]));
+  return fmaxf(fmaxf(m0, m1), m2);
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 tiles.  A 16-lane DPP row owns one tile (8 elements per lane); a wave
+// handles 4 consecutive tiles per step and kU steps, all loads issued before
+// the first use.  Tile t is row t / KB, column block t % KB, and its scale
+// sits at scale[t] (the scale array is dense [rows, KB]).
+constexpr int kActU = 4;
+
+template <bool kBf16, int kU>
+__global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int64_t ld_x,
+                                                          uint32_t n_tiles, FastDiv per_row,
+                                                          uint8_t* __restrict__ q, int64_t ld_q,
+                                                          float* __restrict__ scale) {
+  constexpr int kElt = kBf16 ? 2 : 4;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t sub = lane & 15u;
+  const uint32_t slot = lane >> 4;
+  const uint32_t wave = blockIdx.x * 4u + (threadIdx.x >> 6);
+  const uint32_t base = wave * (4u * kU);
+
+  float v[kU][8];
+  uint32_t tile[kU], row[kU], kb[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    uint32_t t = base + 4u * u + slot;
+    tile[u] = t;
+    t = t < n_tiles ? t : n_tiles - 1;          // clamp: every lane stays active
+    row[u] = per_row.div(t);
+    kb[u] = t - row[u] * per_row.d;
+    const char* p = static_cast<const char*>(x) +
+                    (int64_t(row[u]) * ld_x + int64_t(kb[u]) * 128 + sub * 8) * kElt;
+    load8<kBf16>(p, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const float amax = row16_max(absmax8(v[u]));
+    const float s = tile_scale(amax);
+    const float r = 1.0f / s;
+    const uint2 codes = encode8<kBf16>(v[u], s, r);
+    if (tile[u] < n_tiles) {
+      uint8_t* dst = q + int64_t(row[u]) * ld_q + int64_t(kb[u]) * 128 + sub * 8;
+      *reinterpret_cast<uint2*>(dst) = codes;
+      if (sub == 0) scale[tile[u]] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x1 tiles with transposed output.  A workgroup takes a 128-row x 64-column
+// block of x, stages it in LDS as float32 (row pitch 66 floats), then thread
+// (column pair cp, 16-row group j) reads its 2 x 16 values, the 8 row groups
+// of a column reduce their amax (4 inside the wave, 2 waves through LDS), and
+// each thread writes 16 codes per column: 16 contiguous bytes of the
+// transposed output row.
+constexpr int kTPitch = 66;
+
+template <bool kBf16>
+__global__ __launch_bounds__(256) void quant_128x1_t_kernel(const void* __restrict__ x, int64_t ld_x,
+                                                            int64_t rows, int64_t cols,
+                                                            uint8_t* __restrict__ q, int64_t ld_q,
+                                                            float* __restrict__ scale) {
+  __shared__ float tile[128 * kTPitch];
+  __shared__ float part[2][64];
+  constexpr int kElt = kBf16 ? 2 : 4;
+  const int64_t c0 = int64_t(blockIdx.x) * 64;
+  const int64_t r0 = int64_t(blockIdx.y) * 128;
+  const char* xb = static_cast<const char*>(x);
+
+  // Phase 1: 128 rows x 64 columns as 8-element chunks, 8 chunks per row.
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int chunk = threadIdx.x + 256 * p;
+    const int r = chunk >> 3;
+    const int cc = (chunk & 7) * 8;
+    float v[8];
+    const int64_t col = c0 + cc;
+    const char* src = xb + ((r0 + r) * ld_x + col) * kElt;
+    if (col + 8 <= cols) {
+      load8<kBf16>(src, v);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float f = 0.0f;
+        if (col + i < cols) {
+          if constexpr (kBf16)
+            f = __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(src)[i]) << 16);
+          else
+            f = reinterpret_cast<const float*>(src)[i];
+        }
+        v[i] = f;
+      }
+    }
+    float2* dst = reinterpret_cast<float2*>(&tile[r * kTPitch + cc]);
+    dst[0] = make_float2(v[0], v[1]);
+    dst[1] = make_float2(v[2], v[3]);
+    dst[2] = make_float2(v[4], v[5]);
+    dst[3] = make_float2(v[6], v[7]);
+  }
+  __syncthreads();
+
+  // Phase 2.
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int cp = (lane & 15) + 16 * (w & 1);
+  const int j = (lane >> 4) + 4 * (w >> 1);
+  float a[16], b[16];
+  float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float2 t = *reinterpret_cast<const float2*>(&tile[(16 * j + i) * kTPitch + 2 * cp]);
+    a[i] = t.x;
+    b[i] = t.y;
+    m0 = fmaxf(m0, fabsf(t.x));
+    m1 = fmaxf(m1, fabsf(t.y));
+  }
+  m0 = fmaxf(m0, __shfl_xor(m0, 16));
+  m0 = fmaxf(m0, __shfl_xor(m0, 32));
+  m1 = fmaxf(m1, __shfl_xor(m1, 16));
+  m1 = fmaxf(m1, __shfl_xor(m1, 32));
+  if ((lane >> 4) == 0) {
+    part[w >> 1][2 * cp] = m0;
+    part[w >> 1][2 * cp + 1] = m1;
+  }
+  __syncthreads();
+  m0 = fmaxf(part[0][2 * cp], part[1][2 * cp]);
+  m1 = fmaxf(part[0][2 * cp + 1], part[1][2 * cp + 1]);
+
+  const int64_t kbt = rows / 128;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t col = c0 + 2 * cp + h;
+    const float* val = h ? b : a;
+    const float s = tile_scale(h ? m1 : m0);
+    const float r = 1.0f / s;
+    float qv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qv[i] = quotient<kBf16>(val[i], s, r);
+    if (col < cols) {
+      uint4 out;
+      out.x = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+      out.y = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
+      out.z = pack4_e4m3(qv[8], qv[9], qv[10], qv[11]);
+      out.w = pack4_e4m3(qv[12], qv[13], qv[14], qv[15]);
+      *reinterpret_cast<uint4*>(q + col * ld_q + r0 + 16 * j) = out;
+      if (j == 0) scale[col * kbt + blockIdx.y] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 blocks.  One workgroup per block: thread t holds rows
+// (t/16) + 16p (p < 8), columns 8*(t%16)..+8, i.e. 64 values in registers.
+// Block amax: per-thread max, wave max, then the 4 waves through LDS.  With
+// the transposed copy requested, the codes go through LDS (row pitch 132
+// bytes) and each thread transposes one 8x8 byte sub-block with byte
+// permutes, writing 8-byte pieces of the transposed rows.
+constexpr int kCPitch = 132;  // bytes
+
+__device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                                   uint32_t& o0, uint32_t& o1, uint32_t& o2,
+                                                   uint32_t& o3) {
+  // v_perm_b32(a, b, sel): selector byte values 0..3 pick bytes of b, 4..7 bytes of a.
+  const uint32_t t01l = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+  const uint32_t t01h = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+  const uint32_t t23l = __builtin_amdgcn_perm(w3, w2, 0x05010400u);
+  const uint32_t t23h = __builtin_amdgcn_perm(w3, w2, 0x07030602u);
+  o0 = __builtin_amdgcn_perm(t23l, t01l, 0x05040100u);
+  o1 = __builtin_amdgcn_perm(t23l, t01l, 0x07060302u);
+  o2 = __builtin_amdgcn_perm(t23h, t01h, 0x05040100u);
+  o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
+}
+
+template <bool kBf16, bool kTrans>
+__global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restrict__ w, int64_t ld_w,
+                                                            int64_t rows, int64_t cols,
+                                                            uint8_t* __restrict__ q, int64_t ld_q,
+                                                            float* __restrict__ scale,
+                                                            uint8_t* __restrict__ q_t, int64_t ld_qt,
+                                                            float* __restrict__ scale_t) {
+  __shared__ float red[4];
+  __shared__ uint32_t ct[kTrans ? 128 * kCPitch / 4 : 1];
+  constexpr int kElt = kBf16 ? 2 : 4;
+  const int64_t c0 = int64_t(blockIdx.x) * 128;
+  const int64_t r0 = int64_t(blockIdx.y) * 128;
+  const int t = threadIdx.x;
+  const int cc = (t & 15) * 8;
+  const int rbase = t >> 4;
+
+  float v[8][8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const char* src = static_cast<const char*>(w) + ((r0 + rbase + 16 * p) * ld_w + c0 + cc) * kElt;
+    load8<kBf16>(src, v[p]);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) m = fmaxf(m, absmax8(v[p]));
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = tile_scale(m);
+  const float r = 1.0f / s;
+
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const uint2 codes = encode8<kBf16>(v[p], s, r);
+    const int rr = rbase + 16 * p;
+    *reinterpret_cast<uint2*>(q + (r0 + rr) * ld_q + c0 + cc) = codes;
+    if constexpr (kTrans) {
+      ct[(rr * kCPitch + cc) / 4] = codes.x;
+      ct[(rr * kCPitch + cc) / 4 + 1] = codes.y;
+    }
+  }
+  if (t == 0) {
+    scale[blockIdx.y * (cols / 128) + blockIdx.x] = s;
+    if (scale_t) scale_t[blockIdx.x * (rows / 128) + blockIdx.y] = s;
+  }
+  if constexpr (kTrans) {
+    __syncthreads();
+    const int lane = t & 63;
+    const int a = (lane & 7) | ((lane >> 5) << 3);        // row octet 0..15
+    const int b = ((lane >> 3) & 3) | ((t >> 6) << 2);    // column octet 0..15
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = ((8 * a + i) * kCPitch + 8 * b) / 4;
+      lo[i] = ct[idx];
+      hi[i] = ct[idx + 1];
+    }
+    uint32_t col_lo[8], col_hi[8];   // column j: rows 0-3 in col_lo[j], rows 4-7 in col_hi[j]
+    transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3], col_lo[0], col_lo[1], col_lo[2], col_lo[3]);
+    transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7], col_hi[0], col_hi[1], col_hi[2], col_hi[3]);
+    transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3], col_lo[4], col_lo[5], col_lo[6], col_lo[7]);
+    transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], col_hi[4], col_hi[5], col_hi[6], col_hi[7]);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      uint8_t* dst = q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a;
+      *reinterpret_cast<uint2*>(dst) = make_uint2(col_lo[jj], col_hi[jj]);
+    }
+  }
+}
+
+fp8bs_status check_matrix(const void* p, int64_t ld, int64_t cols, int elt, const char* name) {
+  if (ld < cols) return fail(FP8BS_ERR_INVALID_ARG, "%s: pitch %lld < columns %lld", name, (long long)ld, (long long)cols);
+  if (!aligned16(p) || (ld * elt) % 16 != 0)
+    return fail(FP8BS_ERR_ALIGNMENT, "%s: pointer and row pitch must be 16-byte aligned", name);
+  return FP8BS_OK;
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+using namespace fp8bs;
+
+extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                            int64_t ld_x, int32_t tiling, uint8_t* q, int64_t ld_q,
+                                            float* scale, hipStream_t stream) {
+  const char* fn = "fp8_quant_act_1x128";
+  if (!valid_dtype(x_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown x_dtype %d", fn, x_dtype);
+  if (tiling != FP8BS_TILE_1x128 && tiling != FP8BS_TILE_128x1_T)
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown tiling %d", fn, tiling);
+  if (rows < 0 || cols < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
+  const bool t128x1 = tiling == FP8BS_TILE_128x1_T;
+  if (!t128x1 && cols % 128) return fail(FP8BS_ERR_SHAPE, "%s: cols %lld not a multiple of 128", fn, (long long)cols);
+  if (t128x1 && rows % 128) return fail(FP8BS_ERR_SHAPE, "%s: 128x1 tiling needs rows %% 128 == 0 (rows %lld)", fn, (long long)rows);
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x || !q || !scale) return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const int elt = elem_size(x_dtype);
+  fp8bs_status st = check_matrix(x, ld_x, cols, elt, "x");
+  if (st != FP8BS_OK) return st;
+  st = check_matrix(q, ld_q, t128x1 ? rows : cols, 1, "q");
+  if (st != FP8BS_OK) return st;
+  if (!aligned4(scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
+
+  const bool bf16 = x_dtype == FP8BS_BF16;
+  if (!t128x1) {
+    const int64_t kb = cols / 128;
+    const int64_t n_tiles = rows * kb;
+    if (n_tiles > (int64_t(1) << 31)) return fail(FP8BS_ERR_INVALID_ARG, "%s: more than 2^31 tiles", fn);
+    const int64_t tiles_per_block = 4 * 4 * kActU;   // 4 waves x 4 tiles x kActU steps
+    const dim3 grid(static_cast<uint32_t>((n_tiles + tiles_per_block - 1) / tiles_per_block));
+    const FastDiv per_row(static_cast<uint32_t>(kb));
+    if (bf16)
+      hipLaunchKernelGGL((quant_1x128_kernel<true, kActU>), grid, dim3(256), 0, stream, x, ld_x,
+                         static_cast<uint32_t>(n_tiles), per_row, q, ld_q, scale);
+    else
+      hipLaunchKernelGGL((quant_1x128_kernel<false, kActU>), grid, dim3(256), 0, stream, x, ld_x,
+                         static_cast<uint32_t>(n_tiles), per_row, q, ld_q, scale);
+  } else {
+    if ((cols + 63) / 64 > 0x7fffffff || rows / 128 > 65535)
+      return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles for the launch grid", fn);
+    const dim3 grid(static_cast<uint32_t>((cols + 63) / 64), static_cast<uint32_t>(rows / 128));
+    if (bf16)
+      hipLaunchKernelGGL((quant_128x1_t_kernel<true>), grid, dim3(256), 0, stream, x, ld_x, rows, cols, q, ld_q, scale);
+    else
+      hipLaunchKernelGGL((quant_128x1_t_kernel<false>), grid, dim3(256), 0, stream, x, ld_x, rows, cols, q, ld_q, scale);
+  }
+  return check_launch(fn);
+}
+
+extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,
+                                            int64_t ld_w, uint8_t* q, int64_t ld_q, float* scale,
+                                            uint8_t* q_t, int64_t ld_qt, float* scale_t,
+                                            hipStream_t stream) {
+  const char* fn = "fp8_quant_w_128x128";
+  if (!valid_dtype(w_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown w_dtype %d", fn, w_dtype);
+  if (rows < 0 || cols < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (rows % 128 || cols % 128)
+    return fail(FP8BS_ERR_SHAPE, "%s: rows %lld and cols %lld must be multiples of 128", fn, (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!w || !q || !scale) return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fp8bs_status st = check_matrix(w, ld_w, cols, elem_size(w_dtype), "w");
+  if (st != FP8BS_OK) return st;
+  st = check_matrix(q, ld_q, cols, 1, "q");
+  if (st != FP8BS_OK) return st;
+  if (q_t) {
+    st = check_matrix(q_t, ld_qt, rows, 1, "q_t");
+    if (st != FP8BS_OK) return st;
+  }
+  if (!aligned4(scale) || (scale_t && !aligned4(scale_t)))
+    return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
+  if (rows / 128 > 65535) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many block rows", fn);
+  const dim3 grid(static_cast<uint32_t>(cols / 128), static_cast<uint32_t>(rows / 128));
+  const bool bf16 = w_dtype == FP8BS_BF16;
+  if (bf16 && q_t)
+    hipLaunchKernelGGL((quant_128x128_kernel<true, true>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  else if (bf16)
+    hipLaunchKernelGGL((quant_128x128_kernel<true, false>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  else if (q_t)
+    hipLaunchKernelGGL((quant_128x128_kernel<false, true>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  else
+    hipLaunchKernelGGL((quant_128x128_kernel<false, false>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  return check_launch(fn);
+}

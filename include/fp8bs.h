@@ -1,0 +1,164 @@
+/*
+ * fp8bs.h - fine-grained FP8 (E4M3) block-scaled quantization and GEMM on
+ * AMD MI355X (gfx950).  C ABI of libfp8bs.so.
+ *
+ * The method (sources cited per call below):
+ *  - codingmall.com knowledge-base article on the role of FP8 precision in
+ *    DeepSeek-V3 training, section "Finkornig kvantisering": activations are
+ *    scaled per 1x128 tile and weights per 128x128 block; section
+ *    "Online-kvantisering": each scale comes from its own tile's current
+ *    values; section "Ökad ackumuleringsprecision": GEMM partial sums are
+ *    promoted into FP32 at fixed intervals; section "Unified E4M3 Format":
+ *    E4M3 for every GEMM operand, forward and backward.
+ *  - HolySheep AI (zh) article on FP8 mixed-precision training at
+ *    DeepSeek-671B scale, section "2.2 细粒度量化实现" (fine-grained
+ *    quantization implementation), class FP8BlockQuantizer: per tile,
+ *    scale = amax / 448 (a scale not above 1e-10 becomes 1), codes = E4M3 of
+ *    x / scale, the FP32 scale is returned beside the codes, and
+ *    dequantization multiplies by it.
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls, never synchronizes and
+ *    enqueues its work on `stream` (0 = the null stream).
+ *  - Matrices are row-major.  `ld_*` is the row pitch in ELEMENTS.  E4M3
+ *    codes are uint8 (OCP E4M3FN: bias 7, max 448 = 0x7E, no infinity,
+ *    S.1111.111 = NaN).  Scales are float32 and dense (row pitch = number of
+ *    scale columns).
+ *  - Validation is synchronous.  On any non-OK status nothing is enqueued and
+ *    no output byte is written; fp8bs_last_error() gives the reason.
+ *    Device-side faults surface at the caller's next synchronization.
+ *  - Zero rows (or M = 0) is a no-op that returns FP8BS_OK.
+ *  - Alignment: every code/input/output pointer 16-byte aligned and every
+ *    row pitch a multiple of 16 bytes; scale pointers 4-byte aligned.
+ *  - Quantization rounds to nearest (ties to even) and saturates at +-448; it
+ *    never reports a range error.  Inputs must be finite (NaN/Inf inputs
+ *    give unspecified codes).
+ *  - Tiled dimensions must be whole multiples of 128 (FP8BS_ERR_SHAPE);
+ *    partial tail tiles are rejected, not dropped.
+ *  - Thread-safe: the only global state is the thread-local error text.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fp8bs_status {
+  FP8BS_OK = 0,
+  FP8BS_ERR_INVALID_ARG = 1,   /* null pointer, negative size, pitch too small, bad enum */
+  FP8BS_ERR_SHAPE = 2,         /* a tiled dimension is not a multiple of 128, or K < 128 */
+  FP8BS_ERR_ALIGNMENT = 3,     /* pointer or pitch not aligned as required */
+  FP8BS_ERR_UNSUPPORTED = 4,   /* valid enum values in a combination not provided */
+  FP8BS_ERR_HIP = 5            /* the HIP runtime refused the launch */
+} fp8bs_status;
+
+typedef enum fp8bs_dtype { FP8BS_BF16 = 0, FP8BS_F32 = 1 } fp8bs_dtype;
+
+typedef enum fp8bs_act_tiling {
+  FP8BS_TILE_1x128 = 0,        /* 128 consecutive elements of a row */
+  FP8BS_TILE_128x1_T = 1       /* 128 consecutive rows of a column; codes written transposed */
+} fp8bs_act_tiling;
+
+typedef enum fp8bs_bscale_kind {
+  FP8BS_BSCALE_BLOCK128 = 0,   /* b_scale[N/128][K/128]: one scale per 128x128 block of B */
+  FP8BS_BSCALE_ROW = 1         /* b_scale[N][K/128]: one scale per row of B and 128-K block */
+} fp8bs_bscale_kind;
+
+/*
+ * Online activation quantization (codingmall "Finkornig kvantisering" /
+ * "Online-kvantisering"; HolySheep (zh) section 2.2, FP8BlockQuantizer).
+ *
+ * x:       [rows, cols] of x_dtype (bf16 or f32), pitch ld_x >= cols.
+ * tiling = FP8BS_TILE_1x128: needs cols % 128 == 0.
+ *     q     [rows, cols] uint8, pitch ld_q >= cols;
+ *     scale [rows, cols/128] float32.
+ * tiling = FP8BS_TILE_128x1_T (operands of the weight-gradient GEMM, whose
+ *   contraction runs over rows/tokens): needs rows % 128 == 0.
+ *     q     [cols, rows] uint8 = codes of x^T, pitch ld_q >= rows;
+ *     scale [cols, rows/128] float32.
+ * Per tile: s = fl32(amax/448), s = 1 if not s > fl32(1e-10);
+ * code = E4M3_RNE_SAT(fl32(x/s)).  Codes and scales are bit-exact with that
+ * definition.
+ */
+fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                 int64_t ld_x, int32_t tiling, uint8_t* q, int64_t ld_q,
+                                 float* scale, hipStream_t stream);
+
+/*
+ * Weight quantization in 128x128 blocks (codingmall "Finkornig
+ * kvantisering"; HolySheep (zh) section 2.2 rule applied per block).
+ *
+ * w:       [rows, cols] of w_dtype, pitch ld_w >= cols; rows % 128 == 0 and
+ *          cols % 128 == 0.
+ * q:       [rows, cols] uint8, pitch ld_q >= cols.
+ * scale:   [rows/128, cols/128] float32.
+ * q_t:     optional (may be NULL): the same codes transposed, [cols, rows],
+ *          pitch ld_qt >= rows (the B operand of the data-gradient GEMM).
+ * scale_t: optional (may be NULL): scale transposed, [cols/128, rows/128].
+ */
+fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,
+                                 int64_t ld_w, uint8_t* q, int64_t ld_q, float* scale,
+                                 uint8_t* q_t, int64_t ld_qt, float* scale_t,
+                                 hipStream_t stream);
+
+/*
+ * Block-scaled FP8 GEMM with FP32 promotion per 128-deep K block
+ * (codingmall "Ökad ackumuleringsprecision"):
+ *   y[m,n] = sum_kb  a_scale[m,kb] * bs(n,kb) * P_kb[m,n],
+ *   P_kb[m,n] = sum_{k in block kb} e4m3(a[m,k]) * e4m3(b[n,k])
+ * where P_kb comes from FP8 matrix-core instructions accumulating in FP32 and
+ * the promotion is an FP32 multiply-add per K block.
+ *
+ * a:       [M, K] codes, pitch lda >= K;  a_scale [M, K/128] float32.
+ * b:       [N, K] codes, pitch ldb >= K (y = A . B^T).
+ * b_scale: BLOCK128: [N/128, K/128] (needs N % 128 == 0);
+ *          ROW:      [N, K/128].
+ * y:       [M, N] of y_dtype (f32, or bf16 rounded to nearest even), pitch
+ *          ldy >= N.
+ * K % 128 == 0 and K >= 128; N % 16 == 0.  M may be any count >= 0.
+ * Accuracy: |y - exact| <= 2e-5 * sum_k |a_k b_k| (+ half a bf16 ulp).
+ */
+fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
+                                  const uint8_t* a, int64_t lda, const float* a_scale,
+                                  const uint8_t* b, int64_t ldb, const float* b_scale,
+                                  int32_t b_kind, void* y, int32_t y_dtype, int64_t ldy,
+                                  hipStream_t stream);
+
+/*
+ * Grouped (mixture-of-experts) block-scaled GEMM: group g owns rows
+ * [off[g], off[g+1]) of a and y and has its own weight b[g]
+ * (HolySheep (zh) MoE module: each expert multiplies its own tokens).
+ *
+ * off:     DEVICE int32 [G+1], off[0] = 0, nondecreasing, off[G] = M_total.
+ *          Not read on the host.  The kernel clamps every offset into
+ *          [0, M_total] and treats a decrease as an empty group, so a bad
+ *          table cannot cause an out-of-bounds access (its rows are then
+ *          simply not computed).
+ * a:       [M_total, K] codes (dense, pitch K);  a_scale [M_total, K/128].
+ * b:       [G, N, K] codes (dense);  b_scale [G, N/128, K/128] (BLOCK128).
+ * y:       [M_total, N] of y_dtype (dense, pitch N).  Rows of empty groups
+ *          are not written.
+ * N % 128 == 0, K % 128 == 0, K >= 128, 1 <= G <= 1024.
+ */
+fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t G,
+                                          const int32_t* off, const uint8_t* a,
+                                          const float* a_scale, const uint8_t* b,
+                                          const float* b_scale, void* y, int32_t y_dtype,
+                                          hipStream_t stream);
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* fp8bs_last_error(void);
+
+/* Library version string. */
+const char* fp8bs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

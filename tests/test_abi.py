@@ -1,0 +1,115 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function the header declares, and rejects bad arguments synchronously with the
+documented status (these paths never reach the HIP runtime)."""
+import ctypes
+
+import pytest
+
+import fp8_block_scaled_05_amd as fb
+
+OK, INVALID, SHAPE, ALIGN = 0, 1, 2, 3
+A16 = 0x10000          # a fake, 16-byte aligned "device" address; never dereferenced
+A4 = 0x10004
+NULL = 0
+
+
+@pytest.fixture(scope="module")
+def L():
+    return fb.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = fb.header_functions()
+    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_blockscaled_gemm",
+                          "fp8_blockscaled_grouped_gemm", "fp8bs_last_error", "fp8bs_version"}
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in fb.version()
+
+
+def _act(L, x=A16, dt=0, rows=4, cols=256, ldx=256, tiling=0, q=A16, ldq=256, s=A16):
+    return L.fp8_quant_act_1x128(x, dt, rows, cols, ldx, tiling, q, ldq, s, None)
+
+
+def test_quant_act_validation(L):
+    assert _act(L, rows=0) == OK and _act(L, cols=0) == OK            # empty: no-op
+    assert _act(L, rows=0, x=NULL, q=NULL, s=NULL) == OK
+    assert _act(L, dt=7) == INVALID
+    assert _act(L, tiling=5) == INVALID
+    assert _act(L, rows=-1) == INVALID
+    assert _act(L, cols=200, ldx=256) == SHAPE
+    assert _act(L, tiling=1, rows=100) == SHAPE                       # 128x1 needs rows%128
+    assert _act(L, x=NULL) == INVALID and _act(L, s=NULL) == INVALID
+    assert "null" in fb.last_error()
+    assert _act(L, ldx=128) == INVALID                                 # pitch < cols
+    assert _act(L, x=A16 + 8) == ALIGN
+    assert _act(L, ldx=260) == ALIGN                                   # 520 B rows
+    assert _act(L, q=A16 + 4) == ALIGN
+    assert _act(L, ldq=264) == ALIGN
+    assert _act(L, s=A16 + 2) == ALIGN
+    assert _act(L, tiling=1, rows=128, cols=8, ldx=8, ldq=136) == ALIGN  # q pitch 136 B
+    assert _act(L, tiling=1, rows=128, cols=8, ldx=8, ldq=64) == INVALID  # q pitch < rows
+
+
+def _w(L, w=A16, dt=0, rows=256, cols=256, ldw=256, q=A16, ldq=256, s=A16, qt=NULL, ldqt=0,
+       st=NULL):
+    return L.fp8_quant_w_128x128(w, dt, rows, cols, ldw, q, ldq, s, qt, ldqt, st, None)
+
+
+def test_quant_w_validation(L):
+    assert _w(L, rows=0) == OK
+    assert _w(L, rows=200) == SHAPE and _w(L, cols=100) == SHAPE
+    assert _w(L, dt=3) == INVALID
+    assert _w(L, q=NULL) == INVALID
+    assert _w(L, w=A16 + 4) == ALIGN
+    assert _w(L, qt=A16, ldqt=128) == INVALID                           # ld_qt < rows
+    assert _w(L, qt=A16, ldqt=264) == ALIGN
+    assert _w(L, s=A16 + 1) == ALIGN
+    assert _w(L, qt=A16, ldqt=256, st=A4 + 1) == ALIGN
+
+
+def _gemm(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, y=A16,
+          ydt=1, ldy=256):
+    return L.fp8_blockscaled_gemm(M, N, K, a, lda, sa, b, ldb, sb, kind, y, ydt, ldy, None)
+
+
+def test_gemm_validation(L):
+    assert _gemm(L, M=0) == OK
+    assert _gemm(L, M=0, a=NULL, y=NULL) == OK
+    assert _gemm(L, K=100, lda=112, ldb=112) == SHAPE
+    assert _gemm(L, K=0) == SHAPE
+    assert _gemm(L, N=144, ldy=144) == SHAPE                            # block128 needs N%128
+    assert _gemm(L, N=24, ldy=32, kind=1) == SHAPE                      # N % 16
+    assert _gemm(L, kind=2) == INVALID and _gemm(L, ydt=9) == INVALID
+    assert _gemm(L, M=-3) == INVALID
+    assert _gemm(L, sa=NULL) == INVALID
+    assert _gemm(L, lda=128) == INVALID and _gemm(L, ldy=128) == INVALID
+    assert _gemm(L, a=A16 + 8) == ALIGN and _gemm(L, lda=264) == ALIGN
+    assert _gemm(L, ydt=0, ldy=260) == ALIGN                            # bf16 pitch 520 B
+    assert _gemm(L, sb=A16 + 2) == ALIGN
+
+
+def _grouped(L, M=256, N=256, K=256, G=4, off=A16, a=A16, sa=A16, b=A16, sb=A16, y=A16, ydt=0):
+    return L.fp8_blockscaled_grouped_gemm(M, N, K, G, off, a, sa, b, sb, y, ydt, None)
+
+
+def test_grouped_validation(L):
+    assert _grouped(L, M=0) == OK
+    assert _grouped(L, G=0) == INVALID and _grouped(L, G=2000) == INVALID
+    assert _grouped(L, N=144) == SHAPE and _grouped(L, K=64) == SHAPE
+    assert _grouped(L, off=NULL) == INVALID
+    assert _grouped(L, off=A16 + 2) == ALIGN and _grouped(L, a=A16 + 4) == ALIGN
+    assert _grouped(L, ydt=4) == INVALID
+
+
+def test_last_error_is_per_call_text(L):
+    assert _gemm(L, K=100, lda=112, ldb=112) == SHAPE
+    assert "K=100" in fb.last_error()
+    assert _w(L, rows=200) == SHAPE
+    assert "200" in fb.last_error()
+
+
+def test_binding_raises_typed_error():
+    with pytest.raises(fb.Fp8bsError) as e:
+        fb._check(2)
+    assert e.value.status == 2

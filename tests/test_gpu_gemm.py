@@ -1,0 +1,271 @@
+"""GPU parity of the block-scaled GEMMs against the float64 oracle:
+|y - Y| <= 2e-5 * sum|a_k b_k| per element (+ half a bf16 ulp for bf16 out),
+bit-exact where every intermediate is exact in fp32, on the five workloads
+(full outputs or seeded row samples) and on edge cases."""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_block_scaled_05_amd import synth
+from gpu_util import banner, inputs, dev_bf16, host, f32
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+fb = pytest.importorskip("fp8_block_scaled_05_amd")
+
+ONE = 0x38
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _y_host(y):
+    if y.dtype == torch.bfloat16:
+        return f32(host(y)).astype(np.float64)
+    return host(y).astype(np.float64)
+
+
+def _check_tol(y, ref, bound, out, what):
+    ok = oracle.gemm_tolerance_ok(y, ref, bound, out)
+    if not np.all(ok):
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} of {ok.size} outside tolerance; first {i}: "
+                             f"gpu {y[i]!r} oracle {ref[i]!r} bound {bound[i]!r}")
+
+
+def _quantize_pair(xbits, wbits):
+    a, sa = fb.fp8_quant_act_1x128(dev_bf16(xbits))
+    b, sb, _, _ = fb.fp8_quant_w_128x128(dev_bf16(wbits))
+    return a, sa, b, sb
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("workload,out", [(1, "f32"), (2, "f32"), (2, "bf16")])
+def test_gemm_full(workload, out):
+    d = inputs(workload)
+    banner(f"gemm workload {workload} full, out {out}")
+    a, sa, b, sb = _quantize_pair(d["X"], d["W"])
+    y = fb.fp8_blockscaled_gemm(a, sa, b, sb, "block128",
+                                torch.float32 if out == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, bound = oracle.blockscaled_gemm_ref(host(a), host(sa), host(b), host(sb))
+    _check_tol(_y_host(y), ref, bound, out, f"workload {workload}")
+
+
+def test_gemm_workload3_sampled_rows():
+    d = inputs(3)
+    banner("gemm workload 3 [8192,18432,7168], sampled rows")
+    a, sa, b, sb = _quantize_pair(d["X"], d["W"])
+    y = fb.fp8_blockscaled_gemm(a, sa, b, sb, "block128", torch.float32)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(a.shape[0], 192, seed=3, must=[0, a.shape[0] - 1])
+    ah, sah = host(a)[rows], host(sa)[rows]
+    ref, bound = oracle.blockscaled_gemm_ref(ah, sah, host(b), host(sb))
+    _check_tol(_y_host(y)[rows], ref, bound, "f32", "workload 3")
+
+
+def test_grouped_workload4_sampled_rows():
+    d = inputs(4)
+    off = d["offsets"]
+    g, n, k = d["W"].shape
+    banner(f"grouped gemm workload 4, counts {d['counts'].tolist()}")
+    a, sa = fb.fp8_quant_act_1x128(dev_bf16(d["X"]))
+    b, sb, _, _ = fb.fp8_quant_w_128x128(dev_bf16(d["W"].reshape(g * n, k)))
+    b = b.view(g, n, k)
+    sb = sb.view(g, n // 128, k // 128)
+    y = fb.fp8_blockscaled_grouped_gemm(_dev(off), a, sa, b, sb, torch.bfloat16)
+    torch.cuda.synchronize()
+    must = [int(o) for o in off[:-1] if o < off[-1]] + [int(o) - 1 for o in off[1:] if o > 0]
+    rows = synth.sample_rows(a.shape[0], 160, seed=4, must=must)
+    yh = _y_host(y)
+    ah, sah = host(a), host(sa)
+    bh, sbh = host(b), host(sb)
+    expert = np.searchsorted(off, rows, side="right") - 1
+    for e in np.unique(expert):
+        r = rows[expert == e]
+        ref, bound = oracle.blockscaled_gemm_ref(ah[r], sah[r], bh[e], sbh[e])
+        _check_tol(yh[r], ref, bound, "bf16", f"expert {e}")
+
+
+def test_dgrad_workload5():
+    d = inputs(5)
+    banner("dgrad workload 5: dY[8192,2048] x W[2048,7168] -> dX, sampled rows")
+    a, sa = fb.fp8_quant_act_1x128(dev_bf16(d["dY"]))
+    _, _, bt, sbt = fb.fp8_quant_w_128x128(dev_bf16(d["W"]), transpose=True)
+    y = fb.fp8_blockscaled_gemm(a, sa, bt, sbt, "block128", torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(a.shape[0], 256, seed=5, must=[0, a.shape[0] - 1])
+    ref, bound = oracle.blockscaled_gemm_ref(host(a)[rows], host(sa)[rows], host(bt), host(sbt))
+    _check_tol(_y_host(y)[rows], ref, bound, "bf16", "dgrad")
+
+
+def test_wgrad_workload5():
+    d = inputs(5)
+    banner("wgrad workload 5: X^T dY with 128x1 tiles along tokens -> dW fp32 [7168,2048]")
+    xt, sxt = fb.fp8_quant_act_1x128(dev_bf16(d["X"]), "128x1_T")     # [7168, 8192]
+    dyt, sdyt = fb.fp8_quant_act_1x128(dev_bf16(d["dY"]), "128x1_T")  # [2048, 8192]
+    y = fb.fp8_blockscaled_gemm(xt, sxt, dyt, sdyt, "row", torch.float32)
+    torch.cuda.synchronize()
+    rows = synth.sample_rows(xt.shape[0], 192, seed=55, must=[0, xt.shape[0] - 1])
+    ref, bound = oracle.blockscaled_gemm_ref(host(xt)[rows], host(sxt)[rows], host(dyt),
+                                             host(sdyt), "row")
+    _check_tol(_y_host(y)[rows], ref, bound, "f32", "wgrad")
+
+
+# ---------------------------------------------------------------- exact cases
+def _int_codes(rng, shape):
+    """Codes whose values are integers with |v| <= 16 (0, +-1..16)."""
+    vals = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50, 0x51, 0x52, 0x53,
+                     0x54, 0x55, 0x56, 0x57, 0x58], np.uint8)
+    c = rng.choice(vals, size=shape)
+    return c | (rng.integers(0, 2, size=shape, dtype=np.uint8) << 7)
+
+
+@pytest.mark.parametrize("m,n,k,kind,out", [(256, 256, 7168, "block128", "f32"),
+                                            (300, 384, 1024, "row", "f32"),
+                                            (129, 128, 128, "block128", "f32")])
+def test_integer_exact_is_bit_exact(m, n, k, kind, out):
+    rng = np.random.default_rng([20, m, n, k])
+    a = _int_codes(rng, (m, k))
+    b = _int_codes(rng, (n, k))
+    assert np.all(np.abs(oracle.e4m3_decode(a)) <= 16)
+    sa = rng.choice(np.float32([1.0, 2.0]), size=(m, k // 128))
+    sb = rng.choice(np.float32([0.5, 1.0]), size=(n // 128 if kind == "block128" else n, k // 128))
+    banner(f"gemm integer-exact {m}x{n}x{k} {kind}")
+    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), kind, torch.float32)
+    torch.cuda.synchronize()
+    ref, _ = oracle.blockscaled_gemm_ref(a, sa, b, sb, kind)
+    assert np.array_equal(_y_host(y), ref)
+
+
+def test_selection_closed_form():
+    rng = np.random.default_rng(21)
+    m, n, k = 200, 256, 1024
+    perm = rng.permutation(k)[:m]
+    a = np.zeros((m, k), np.uint8)
+    a[np.arange(m), perm] = ONE
+    b = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x30
+    sa = np.ones((m, k // 128), np.float32)
+    sb = np.ones((n // 128, k // 128), np.float32)
+    banner("gemm selection closed form")
+    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), "block128", torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(_y_host(y), oracle.e4m3_decode(b[:, perm]).T)
+
+
+def test_scale_routing_powers_of_two():
+    rng = np.random.default_rng(22)
+    m, n, k = 256, 384, 1024
+    kbs = k // 128
+    a = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+    b = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x38
+    b[(b & 0x7F) == 0x7F] = 0x38
+    sa = np.float32(2.0) ** rng.integers(-20, 21, size=(m, kbs)).astype(np.float32)
+    sb = np.float32(2.0) ** rng.integers(-20, 21, size=(n // 128, kbs)).astype(np.float32)
+    banner("gemm scale routing 2^+-20")
+    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), "block128", torch.float32)
+    torch.cuda.synchronize()
+    ref, bound = oracle.blockscaled_gemm_ref(a, sa, b, sb)
+    _check_tol(_y_host(y), ref, bound, "f32", "scale routing")
+
+
+# ---------------------------------------------------------------- edges
+@pytest.mark.parametrize("m,n,k,kind", [(1, 128, 128, "block128"), (5, 256, 384, "block128"),
+                                        (127, 128, 256, "block128"), (129, 384, 512, "block128"),
+                                        (255, 16, 256, "row"), (33, 144, 640, "row")])
+def test_tails_and_pitches(m, n, k, kind):
+    rng = np.random.default_rng([23, m, n, k])
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
+    a, sa = fb.fp8_quant_act_1x128(dev_bf16(x))
+    b = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x38
+    sb = (rng.random((n // 128 if kind == "block128" else n, k // 128)) + 0.01).astype(np.float32)
+    lda, ldb, ldy = k + 32, k + 16, n + 16
+    abuf = torch.zeros((m, lda), dtype=torch.uint8, device="cuda")
+    abuf[:, :k] = a
+    bbuf = torch.zeros((n, ldb), dtype=torch.uint8, device="cuda")
+    bbuf[:, :k] = _dev(b)
+    ybuf = torch.full((m + 2, ldy), -3.0, dtype=torch.float32, device="cuda")
+    banner(f"gemm tails {m}x{n}x{k} {kind}, pitches {lda}/{ldb}/{ldy}")
+    fb.fp8_blockscaled_gemm(abuf[:, :k], sa, bbuf[:, :k], _dev(sb), kind, y=ybuf[1:m + 1, :n])
+    torch.cuda.synchronize()
+    yb = host(ybuf)
+    ref, bound = oracle.blockscaled_gemm_ref(host(a), host(sa), b, sb, kind)
+    _check_tol(yb[1:m + 1, :n].astype(np.float64), ref, bound, "f32", "tails")
+    assert np.all(yb[0] == -3.0) and np.all(yb[-1] == -3.0) and np.all(yb[:, n:] == -3.0)
+
+
+def test_grouped_edges_and_single_group_equals_dense():
+    rng = np.random.default_rng(24)
+    n, k = 256, 512
+    counts = np.array([0, 1, 130, 0, 127, 256, 0, 3])
+    off = synth.offsets_from_counts(counts)
+    m = int(off[-1])
+    g = len(counts)
+    a = rng.integers(0, 256, size=(m, k), dtype=np.uint8)
+    a[(a & 0x7F) == 0x7F] = 0x38
+    sa = (rng.random((m, k // 128)) + 0.1).astype(np.float32)
+    b = rng.integers(0, 256, size=(g, n, k), dtype=np.uint8)
+    b[(b & 0x7F) == 0x7F] = 0x38
+    sb = (rng.random((g, n // 128, k // 128)) + 0.1).astype(np.float32)
+    banner(f"grouped edges counts {counts.tolist()}")
+    y = fb.fp8_blockscaled_grouped_gemm(_dev(off), _dev(a), _dev(sa), _dev(b), _dev(sb),
+                                        torch.float32)
+    torch.cuda.synchronize()
+    ref, bound = oracle.grouped_gemm_ref(off, a, sa, b, sb)
+    _check_tol(_y_host(y), ref, bound, "f32", "grouped")
+    # one group over all rows gives the same bits as the dense kernel
+    off1 = np.array([0, m], np.int32)
+    y1 = fb.fp8_blockscaled_grouped_gemm(_dev(off1), _dev(a), _dev(sa), _dev(b[:1]),
+                                         _dev(sb[:1]), torch.float32)
+    yd = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b[0]), _dev(sb[0]), "block128",
+                                 torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, yd)
+
+
+def test_grouped_bad_offsets_stay_in_bounds():
+    """A decreasing or out-of-range offset table must not make the kernel touch
+    rows outside [0, M): such groups are clamped (or empty)."""
+    rng = np.random.default_rng(25)
+    n, k, m = 128, 256, 300
+    off = np.array([0, 200, 100, 900, -5, 300], np.int32)
+    a = rng.integers(0, 0x30, size=(m, k), dtype=np.uint8)
+    sa = np.ones((m, 2), np.float32)
+    b = rng.integers(0, 0x30, size=(5, n, k), dtype=np.uint8)
+    sb = np.ones((5, 1, 2), np.float32)
+    ybuf = torch.full((m + 2, n), -3.0, dtype=torch.float32, device="cuda")
+    banner("grouped with a bad offset table")
+    fb.fp8_blockscaled_grouped_gemm(_dev(off), _dev(a), _dev(sa), _dev(b), _dev(sb),
+                                    y=ybuf[1:m + 1])
+    torch.cuda.synchronize()
+    yb = host(ybuf)
+    assert np.all(yb[0] == -3.0) and np.all(yb[-1] == -3.0)
+    # rows 0..199 belong to group 0 and are computed correctly
+    ref, bound = oracle.blockscaled_gemm_ref(a[:200], sa[:200], b[0], sb[0])
+    _check_tol(yb[1:201].astype(np.float64), ref, bound, "f32", "valid group")
+
+
+def test_gemm_repeat_bitwise_identical():
+    d = inputs(1)
+    banner("gemm repeatability")
+    a, sa, b, sb = _quantize_pair(d["X"], d["W"])
+    y1 = fb.fp8_blockscaled_gemm(a, sa, b, sb)
+    y2 = fb.fp8_blockscaled_gemm(a, sa, b, sb)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_gemm_zero_m_is_noop():
+    banner("gemm M=0")
+    a = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    b = torch.zeros((128, 256), dtype=torch.uint8, device="cuda")
+    sb = torch.ones((1, 2), dtype=torch.float32, device="cuda")
+    y = fb.fp8_blockscaled_gemm(a, sa, b, sb)
+    assert y.shape == (0, 128)
