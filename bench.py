@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 M, N, K = 4096, 2048, 7168
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
+PEAK_F16_TFLOPS = 2500.0        # MI355X dense f16/bf16 MFMA (the FP32-accumulating path)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
 
@@ -51,6 +52,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--out", choices=["bf16", "f32"], default="bf16")
+    p.add_argument("--accum", choices=["fp32", "fp8_mfma"], default="fp32",
+                   help="block-partial accumulation of the GEMM (see include/fp8bs.h)")
     p.add_argument("--rotate-mib", type=int, default=1100,
                    help="bytes of input/output buffers cycled through (defeats the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -125,6 +128,7 @@ def main():
     hs = ctypes.c_void_p(stream.cuda_stream)
     vp = ctypes.c_void_p
     ycode = 0 if args.out == "bf16" else 1
+    accum = fb._ACCUM[args.accum]
 
     def step(i):
         """Three library calls on `stream`, with prepared arguments (no per-call checks)."""
@@ -135,7 +139,7 @@ def main():
                                     vp(sb.data_ptr()), None, 0, None, hs)
         st |= L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
                                      vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
-                                     vp(ys[j].data_ptr()), ycode, N, hs)
+                                     vp(ys[j].data_ptr()), ycode, N, accum, hs)
         if st:
             raise RuntimeError(fb.last_error())
 
@@ -167,7 +171,7 @@ def main():
         e[2].record(stream)
         if L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
                                   vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
-                                  vp(ys[j].data_ptr()), ycode, N, hs):
+                                  vp(ys[j].data_ptr()), ycode, N, accum, hs):
             raise RuntimeError(fb.last_error())
         e[3].record(stream)
     end.record(stream)
@@ -180,6 +184,22 @@ def main():
     med_ms = np.median(per, axis=0)
     qx_bytes, qw_bytes, flops = algorithmic()
     gemm_tflops = flops / (avg_ms[2] * 1e-3) / 1e12
+    peak = PEAK_F16_TFLOPS if args.accum == "fp32" else PEAK_FP8_TFLOPS
+
+    # For context: the other accumulation mode's GEMM on the same codes.
+    other = 1 - accum
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(5):
+        L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()), vp(b.data_ptr()), K,
+                               vp(sb.data_ptr()), 0, vp(ys[0].data_ptr()), ycode, N, other, hs)
+    g0.record(stream)
+    n_alt = 50
+    for i in range(n_alt):
+        L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()), vp(b.data_ptr()), K,
+                               vp(sb.data_ptr()), 0, vp(ys[i % n_sets].data_ptr()), ycode, N, other, hs)
+    g1.record(stream)
+    torch.cuda.synchronize()
+    alt_us = g0.elapsed_time(g1) / n_alt * 1e3
     qx_gbps = qx_bytes / (avg_ms[0] * 1e-3) / 1e9
     qw_gbps = qw_bytes / (avg_ms[1] * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12
@@ -203,10 +223,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": "linear layer: quantize X[4096,7168] 1x128 + W[2048,7168] "
                                "128x128, GEMM Y[4096,2048] with FP32 promotion per 128-K block",
-                   "M": M, "N": N, "K": K, "out": args.out, "accumulate": "f32",
+                   "M": M, "N": N, "K": K, "out": args.out, "accum": args.accum,
                    "buffer_sets": n_sets},
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": PEAK_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
                      "traffic": traffic},
         "kernels": {
             "quant_act_1x128": {"avg_us": round(avg_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2),
@@ -215,9 +235,14 @@ def main():
             "quant_w_128x128": {"avg_us": round(avg_ms[1] * 1e3, 2), "median_us": round(med_ms[1] * 1e3, 2),
                                 "GB/s": round(qw_gbps, 1), "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4),
                                 "bytes": qw_bytes},
-            "blockscaled_gemm": {"avg_us": round(avg_ms[2] * 1e3, 2), "median_us": round(med_ms[2] * 1e3, 2),
+            "blockscaled_gemm": {"accum": args.accum, "mfma": "f16" if args.accum == "fp32" else "fp8",
+                                 "avg_us": round(avg_ms[2] * 1e3, 2), "median_us": round(med_ms[2] * 1e3, 2),
                                  "TFLOP/s": round(gemm_tflops, 2),
-                                 "frac_mfma": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "flops": flops},
+                                 "frac_own_peak": round(gemm_tflops / peak, 4),
+                                 "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "flops": flops},
+            "blockscaled_gemm_other_accum": {
+                "accum": "fp8_mfma" if args.accum == "fp32" else "fp32", "avg_us": round(alt_us, 2),
+                "TFLOP/s": round(flops / (alt_us * 1e-6) / 1e12, 2), "launches": n_alt},
         },
     }
     if not args.no_cpu_baseline:

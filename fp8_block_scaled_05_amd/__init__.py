@@ -31,6 +31,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "ALIGNMENT", 4: "UNSUPPORTED
 BF16, F32 = 0, 1
 TILE_1x128, TILE_128x1_T = 0, 1
 BSCALE_BLOCK128, BSCALE_ROW = 0, 1
+ACCUM_FP32, ACCUM_FP8_MFMA = 0, 1
+_ACCUM = {"fp32": ACCUM_FP32, "fp8_mfma": ACCUM_FP8_MFMA}
 
 
 class Fp8bsError(RuntimeError):
@@ -58,8 +60,8 @@ def lib():
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     L.fp8_quant_act_1x128.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
     L.fp8_quant_w_128x128.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
-    L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp]
-    L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, vp]
+    L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, i32, vp]
+    L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     for f in ("fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_blockscaled_gemm",
               "fp8_blockscaled_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int
@@ -195,8 +197,12 @@ def fp8_quant_w_128x128(w, transpose=False, q=None, scale=None, q_t=None, scale_
     return q, scale, q_t, scale_t
 
 
-def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None):
-    """y[M, N] = dequant(a) . dequant(b)^T with FP32 promotion per 128-K block."""
+def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None,
+                         accum="fp32"):
+    """y[M, N] = dequant(a) . dequant(b)^T with FP32 promotion per 128-K block.
+
+    accum "fp32" (default) sums each block's exact products in FP32; "fp8_mfma"
+    uses the FP8 matrix instructions (faster, ~14-bit group accumulation)."""
     torch = _torch()
     _on_gpu(a, a_scale, b, b_scale, y)
     m, k = a.shape
@@ -219,11 +225,13 @@ def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=No
             raise ValueError(f"{nm} must be contiguous")
     _check(lib().fp8_blockscaled_gemm(m, n, k, _ptr(a), _pitch(a, "a"), _ptr(a_scale), _ptr(b),
                                       _pitch(b, "b"), _ptr(b_scale), kind, _ptr(y),
-                                      _dtype_code(y, "y"), _pitch(y, "y"), _stream()))
+                                      _dtype_code(y, "y"), _pitch(y, "y"), _ACCUM[accum],
+                                      _stream()))
     return y
 
 
-def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None, y=None):
+def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None, y=None,
+                                 accum="fp32"):
     """Per-group GEMM: group g owns rows [offsets[g], offsets[g+1]) of a and y,
     multiplied by b[g] ([G, N, K] codes, [G, N/128, K/128] scales)."""
     torch = _torch()
@@ -247,5 +255,5 @@ def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None
     _need(y, (m, n), y.dtype, "y")
     _check(lib().fp8_blockscaled_grouped_gemm(m, n, k, g, _ptr(offsets), _ptr(a), _ptr(a_scale),
                                               _ptr(b), _ptr(b_scale), _ptr(y),
-                                              _dtype_code(y, "y"), _stream()))
+                                              _dtype_code(y, "y"), _ACCUM[accum], _stream()))
     return y

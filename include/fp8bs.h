@@ -70,6 +70,24 @@ typedef enum fp8bs_bscale_kind {
 } fp8bs_bscale_kind;
 
 /*
+ * How the block partials P_kb are accumulated.
+ *
+ * FP8BS_ACCUM_FP32 (the default): each product of two E4M3 values is exact
+ *   and the 128 products of a K block are summed in FP32, so the result
+ *   meets |y - exact| <= 2e-5 * sum_k |a_k b_k|.  The codes are widened to
+ *   f16 (exactly) inside the kernel and multiplied on the f16 matrix cores.
+ * FP8BS_ACCUM_FP8_MFMA: the gfx950 FP8 matrix instructions, at twice the
+ *   peak rate.  They add products in groups of 8 consecutive K and keep only
+ *   the bits down to 2^-13 of each group's largest product (truncating the
+ *   rest) before combining the groups in FP32: an error of up to about
+ *   7 * 2^-13 of the largest product per group of 8.  This is the limited
+ *   matrix-core accumulation precision that the codingmall section "Ökad
+ *   ackumuleringsprecision" describes, here inside every instruction, so
+ *   promoting more often cannot remove it.
+ */
+typedef enum fp8bs_accum { FP8BS_ACCUM_FP32 = 0, FP8BS_ACCUM_FP8_MFMA = 1 } fp8bs_accum;
+
+/*
  * Online activation quantization (codingmall "Finkornig kvantisering" /
  * "Online-kvantisering"; HolySheep (zh) section 2.2, FP8BlockQuantizer).
  *
@@ -111,8 +129,8 @@ fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, i
  * (codingmall "Ökad ackumuleringsprecision"):
  *   y[m,n] = sum_kb  a_scale[m,kb] * bs(n,kb) * P_kb[m,n],
  *   P_kb[m,n] = sum_{k in block kb} e4m3(a[m,k]) * e4m3(b[n,k])
- * where P_kb comes from FP8 matrix-core instructions accumulating in FP32 and
- * the promotion is an FP32 multiply-add per K block.
+ * where P_kb comes from the matrix cores (see fp8bs_accum) and the promotion
+ * is an FP32 multiply-add per K block.
  *
  * a:       [M, K] codes, pitch lda >= K;  a_scale [M, K/128] float32.
  * b:       [N, K] codes, pitch ldb >= K (y = A . B^T).
@@ -120,14 +138,16 @@ fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, i
  *          ROW:      [N, K/128].
  * y:       [M, N] of y_dtype (f32, or bf16 rounded to nearest even), pitch
  *          ldy >= N.
+ * accum:   fp8bs_accum (see above).
  * K % 128 == 0 and K >= 128; N % 16 == 0.  M may be any count >= 0.
- * Accuracy: |y - exact| <= 2e-5 * sum_k |a_k b_k| (+ half a bf16 ulp).
+ * Accuracy with FP8BS_ACCUM_FP32: |y - exact| <= 2e-5 * sum_k |a_k b_k|
+ * (+ half a bf16 ulp for bf16 output).
  */
 fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a, int64_t lda, const float* a_scale,
                                   const uint8_t* b, int64_t ldb, const float* b_scale,
                                   int32_t b_kind, void* y, int32_t y_dtype, int64_t ldy,
-                                  hipStream_t stream);
+                                  int32_t accum, hipStream_t stream);
 
 /*
  * Grouped (mixture-of-experts) block-scaled GEMM: group g owns rows
@@ -143,13 +163,14 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
  * b:       [G, N, K] codes (dense);  b_scale [G, N/128, K/128] (BLOCK128).
  * y:       [M_total, N] of y_dtype (dense, pitch N).  Rows of empty groups
  *          are not written.
+ * accum:   fp8bs_accum, as for fp8_blockscaled_gemm.
  * N % 128 == 0, K % 128 == 0, K >= 128, 1 <= G <= 1024.
  */
 fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t G,
                                           const int32_t* off, const uint8_t* a,
                                           const float* a_scale, const uint8_t* b,
                                           const float* b_scale, void* y, int32_t y_dtype,
-                                          hipStream_t stream);
+                                          int32_t accum, hipStream_t stream);
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* fp8bs_last_error(void);

@@ -69,8 +69,8 @@ def test_quant_w_validation(L):
 
 
 def _gemm(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, y=A16,
-          ydt=1, ldy=256):
-    return L.fp8_blockscaled_gemm(M, N, K, a, lda, sa, b, ldb, sb, kind, y, ydt, ldy, None)
+          ydt=1, ldy=256, accum=0):
+    return L.fp8_blockscaled_gemm(M, N, K, a, lda, sa, b, ldb, sb, kind, y, ydt, ldy, accum, None)
 
 
 def test_gemm_validation(L):
@@ -81,6 +81,7 @@ def test_gemm_validation(L):
     assert _gemm(L, N=144, ldy=144) == SHAPE                            # block128 needs N%128
     assert _gemm(L, N=24, ldy=32, kind=1) == SHAPE                      # N % 16
     assert _gemm(L, kind=2) == INVALID and _gemm(L, ydt=9) == INVALID
+    assert _gemm(L, accum=2) == INVALID and _gemm(L, accum=-1) == INVALID
     assert _gemm(L, M=-3) == INVALID
     assert _gemm(L, sa=NULL) == INVALID
     assert _gemm(L, lda=128) == INVALID and _gemm(L, ldy=128) == INVALID
@@ -89,8 +90,9 @@ def test_gemm_validation(L):
     assert _gemm(L, sb=A16 + 2) == ALIGN
 
 
-def _grouped(L, M=256, N=256, K=256, G=4, off=A16, a=A16, sa=A16, b=A16, sb=A16, y=A16, ydt=0):
-    return L.fp8_blockscaled_grouped_gemm(M, N, K, G, off, a, sa, b, sb, y, ydt, None)
+def _grouped(L, M=256, N=256, K=256, G=4, off=A16, a=A16, sa=A16, b=A16, sb=A16, y=A16, ydt=0,
+             accum=0):
+    return L.fp8_blockscaled_grouped_gemm(M, N, K, G, off, a, sa, b, sb, y, ydt, accum, None)
 
 
 def test_grouped_validation(L):
@@ -99,7 +101,7 @@ def test_grouped_validation(L):
     assert _grouped(L, N=144) == SHAPE and _grouped(L, K=64) == SHAPE
     assert _grouped(L, off=NULL) == INVALID
     assert _grouped(L, off=A16 + 2) == ALIGN and _grouped(L, a=A16 + 4) == ALIGN
-    assert _grouped(L, ydt=4) == INVALID
+    assert _grouped(L, ydt=4) == INVALID and _grouped(L, accum=3) == INVALID
 
 
 def test_last_error_is_per_call_text(L):

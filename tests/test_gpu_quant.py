@@ -114,11 +114,13 @@ def _special_rows(rng, rows, cols):
     x = rng.standard_normal((rows, cols)).astype(np.float32)
     t = x.reshape(rows, cols // 128, 128)
     t[0, 0] = 0.0                                     # zero tile
-    t[0, 1] = -0.0                                    # negative-zero tile
+    if cols >= 256:
+        t[0, 1] = -0.0                                # negative-zero tile
     if cols >= 384:
         t[0, 2] *= np.float32(1e-9)                   # amax/448 under the 1e-10 guard
     if rows > 1:
         t[1, 0] = np.float32(2.0 ** -130) * np.sign(t[1, 0])  # bf16 subnormals
+    if rows > 1 and cols >= 256:
         t[1, 1, :64] *= np.float32(3.0e38 / 5)        # near the top of the bf16 range
         t[1, 1, 64:] *= np.float32(1e-30)             # huge + tiny in one tile
     if rows > 2:
