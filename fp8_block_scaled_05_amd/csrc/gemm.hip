@@ -10,34 +10,39 @@
 // where P_kb is the product of the E4M3 codes over the block.
 //
 // The same limitation exists on gfx950.  Its FP8 matrix instructions
-// (v_mfma_*_f8f6f4 and v_mfma_*_fp8_fp8) add products in groups of 8
-// consecutive K, keeping only the bits down to 2^-13 of the group's largest
-// product and truncating the rest; the groups are then combined in FP32.
-// That is about 14 significant bits - short of the 2e-5 * sum|a*b| accuracy
-// asked of the GEMM on realistic data.  The f16 and bf16 matrix instructions
-// accumulate exact products in FP32, and every E4M3 value is exact in f16.
-// Two kernels therefore share everything but the block product:
+// (v_mfma_*_f8f6f4) add products in groups of 8 consecutive K, keeping only
+// the bits down to 2^-13 of the group's largest product; the groups are then
+// combined in FP32.  That is about 14 significant bits - short of the
+// 2e-5 * sum|a*b| accuracy asked of the GEMM on realistic data.  The f16
+// matrix instructions accumulate exact products in FP32, and every E4M3
+// value is exact in f16.  One kernel template serves both block products:
 //
-//  * FP8BS_ACCUM_FP32 (default): E4M3 tiles are loaded from HBM (1 byte per
-//    element), widened to f16 while being staged into LDS (one
-//    v_cvt_scalef32_pk_f16_fp8 per two codes, exact), and multiplied with
-//    v_mfma_f32_32x32x16_f16, eight per 128-deep block, chained in FP32.
-//  * FP8BS_ACCUM_FP8_MFMA: one v_mfma_f32_16x16x128_f8f6f4 per 16x16 output
-//    sub-tile and K block, straight from E4M3 tiles in LDS; twice the peak
-//    rate, with the accumulation described above.
+//  * FP8BS_ACCUM_FP32 (default): E4M3 tiles go from HBM to LDS unchanged
+//    (1 byte per element); each wave widens the 8-byte K slices it feeds to
+//    the matrix core into f16 in registers (v_cvt_scalef32_pk_f16_fp8, two
+//    codes per instruction, exact) and multiplies them with
+//    v_mfma_f32_32x32x16_f16, eight chained per 128-deep block.
+//  * FP8BS_ACCUM_FP8_MFMA: two v_mfma_f32_32x32x64_f8f6f4 per 32x32 output
+//    and K block, straight from the E4M3 bytes; twice the peak rate, with
+//    the accumulation described above.
 //
-// Common design (one workgroup = 256 threads = 4 waves, output tile 128 x 128,
-// each wave a 64 x 64 quadrant):
-//  * the next K block's global loads are in flight while the current block
-//    is multiplied; LDS is double-buffered, one barrier per block;
-//  * the promotion is one FP32 FMA per output element per K block; the
-//    scale product sa*sb is formed once per row (block128 B scales) or per
-//    element (per-row B scales of the weight-gradient GEMM);
-//  * workgroups are renumbered so that each XCD (which has its own L2) gets
-//    a contiguous range of tiles, walked in groups of 8 M tiles so that a
-//    range shares A rows and B rows in that L2;
-//  * rows beyond M (or beyond a group's end) and columns beyond N are
-//    loaded as zeros and never stored.
+// Structure (dense 256 x 128 output tile, 8 waves of 64 x 64):
+//  * A three-stage LDS ring.  Each stage holds one K block of the A and B
+//    tiles (128 bytes per row) and that block's scales, filled by 16-byte
+//    direct global->LDS buffer loads issued two blocks ahead.  Buffer
+//    addressing returns zeros for rows past the end of A (or of a group) and
+//    past N, so tails need no branches.  Each stage lives in its own LDS
+//    object so the compiler can track which loads a read depends on.
+//  * Rows are stored 128 bytes apart with the 16-byte chunks XOR-swizzled by
+//    (row & 7) ^ ((row >> 3) & 1): the matrix-core reads (16 consecutive
+//    rows, one chunk) hit distinct banks with 32 or 64 banks.
+//  * The B tile is the matrix instruction's first operand and the A tile
+//    its second, so a lane's accumulators share one output row (m) per 32-row
+//    subtile and the promotion needs one sa*sb product per subtile.
+//  * Promotion: one FP32 FMA per output element per K block (two with the
+//    per-row B scales of the weight-gradient GEMM).
+//  * Workgroups are renumbered so that each XCD (own L2) works on a compact
+//    block of output tiles (4 M tiles x 8 N tiles for the 256 x 128 case).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -47,21 +52,57 @@
 #include "status.hpp"
 
 namespace fp8bs {
+
 namespace {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Direct global->LDS buffer loads: lane i's 16 (or 4) bytes at
+// voffset + soffset of the buffer land at LDS byte lds_addr + 16 i (4 i).
+// Offsets outside the buffer read as zero.  Issued from inline asm so the
+// compiler does not track them; the kernel orders them explicitly with
+// s_waitcnt vmcnt + s_barrier before any wave reads the stage they fill.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t lds_addr, int voffset, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
+}
+__device__ __forceinline__ void dma4(i32x4 rsrc, uint32_t lds_addr, int voffset, int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc), "s"(soffset) : "memory");
+}
+
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 128;
-constexpr int kGroupM = 8;           // tile-walk group height (in M tiles)
-constexpr int kThreads = 256;
-constexpr int kPitch8 = 144;         // LDS row pitch of an E4M3 tile, bytes
-constexpr int kPitch16 = 136;        // LDS row pitch of an f16 tile, halves (272 bytes)
+// Buffer resource for `bytes` bytes at `base` (raw, stride 0).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = static_cast<int32_t>(static_cast<uint32_t>(a));
+  r.y = static_cast<int32_t>(static_cast<uint32_t>(a >> 32) & 0xffffu);
+  r.z = static_cast<int32_t>(bytes > 0xffffffffull ? 0xffffffffu : static_cast<uint32_t>(bytes));
+  r.w = 0x00020000;
+  return r;
+}
+
+// 32-bit LDS address of a __shared__ object.
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(const T* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) T*)(p)));
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and all its LDS/scalar reads are done, then barrier.  The asm
+// clobber keeps the compiler from moving memory operations across it.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
 
 struct GemmArgs {
   const uint8_t* a;
@@ -69,20 +110,61 @@ struct GemmArgs {
   const uint8_t* b;
   const float* b_scale;
   void* y;
-  const int32_t* off;      // grouped: [G+1] row offsets (device)
+  const int32_t* off;       // grouped: [G+1] row offsets (device)
   int64_t lda, ldb, ldy;
-  int64_t b_group_stride;  // grouped: bytes between experts' B
-  int64_t bs_group_stride; // grouped: floats between experts' B scales
+  int64_t b_group_stride;   // grouped: bytes between experts' B
+  int64_t bs_group_stride;  // grouped: floats between experts' B scales
   int32_t M, N, KB;
-  int32_t tiles_m, tiles_n;  // tiles_m: real (dense) or virtual upper bound (grouped)
+  int32_t tiles_m, tiles_n;  // tiles_m: real (dense) or an upper bound (grouped)
   int32_t G;
 };
 
-// Workgroup id -> (M tile, N tile).
+template <int BM_, int BN_, int WM_, int WN_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int kWaves = WM * WN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int SM = TM / 32, SN = TN / 32;  // 32 x 32 subtiles per wave
+  static constexpr int kGroupM = 4;                 // tile-walk group height (M tiles)
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 subtiles");
+  static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "tile loads must split evenly");
+  static constexpr int RSA = BM / kWaves, RSB = BN / kWaves;   // scale rows per wave
+  static_assert(RSA <= 64 && 64 % RSA == 0 && RSB <= 64 && 64 % RSB == 0, "scale rows per wave");
+};
+
+// One K block of the A and B tiles and their scales.  Every wave loads the
+// scales of BM / waves rows (and BN / waves per-row B scales) with one 64-lane
+// load into its own 64-float slot, lane i taking row (i % rows-per-wave), so
+// each wave issues the same number of loads per stage.
+template <int BM, int BN, int NW, bool kRowScale>
+struct alignas(16) Stage {
+  uint8_t a[BM * 128];
+  uint8_t b[BN * 128];
+  float sa[NW][64];
+  float sb[kRowScale ? NW : 1][64];
+};
+
+// 16-byte chunk swizzle of a 128-byte LDS row.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Byte offset of logical 16-byte chunk `chunk` of LDS row `row`.
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
+
+__device__ __forceinline__ uint4 lds_read16(const uint8_t* base, int off) {
+  return *reinterpret_cast<const uint4*>(base + off);
+}
+
+// Workgroup id -> (M tile, N tile).  The hardware hands workgroup i to XCD
+// i % 8; renumber so each XCD gets a contiguous range of the tile walk, and
+// walk kGroupM M tiles at a time so a range shares A and B rows in its L2.
+template <int kGroupM>
 __device__ __forceinline__ void tile_of(uint32_t wg, uint32_t n_wg, int tiles_m, int tiles_n,
                                         int& tm, int& tn) {
-  if ((n_wg & 7u) == 0) wg = (wg & 7u) * (n_wg >> 3) + (wg >> 3);   // XCD-contiguous ranges
-  const uint32_t per_group = uint32_t(kGroupM) * tiles_n;
+  const uint32_t q = n_wg >> 3, r = n_wg & 7u;
+  const uint32_t x = wg & 7u;
+  wg = x * q + min(x, r) + (wg >> 3);
+  const uint32_t per_group = uint32_t(kGroupM) * uint32_t(tiles_n);
   const uint32_t g = wg / per_group;
   const uint32_t first_m = g * kGroupM;
   const uint32_t gm = min(uint32_t(tiles_m) - first_m, uint32_t(kGroupM));
@@ -100,13 +182,13 @@ struct Tile {
 
 // Returns false when a grouped workgroup has no tile (uniform across the
 // workgroup, before any barrier).
-template <bool kGrouped>
+template <class C, bool kGrouped>
 __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
   int tm, tn;
-  tile_of(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn);
+  tile_of<C::kGroupM>(blockIdx.x, gridDim.x, args.tiles_m, args.tiles_n, tm, tn);
   tile.bmat = args.b;
   tile.bscale = args.b_scale;
-  tile.n0 = int64_t(tn) * kBN;
+  tile.n0 = int64_t(tn) * C::BN;
   if constexpr (kGrouped) {
     // Find the group holding virtual M tile `tm`; offsets are clamped into
     // [0, M] and a decreasing pair counts as an empty group.
@@ -117,377 +199,296 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
       lo = max(int64_t(0), min(int64_t(args.off[g]), int64_t(args.M)));
       hi = max(int64_t(0), min(int64_t(args.off[g + 1]), int64_t(args.M)));
       if (hi < lo) hi = lo;
-      const int cnt = int((hi - lo + kBM - 1) / kBM);
+      const int cnt = int((hi - lo + C::BM - 1) / C::BM);
       if (vm < cnt) { found = true; break; }
       vm -= cnt;
     }
     if (!found) return false;
-    tile.row0 = lo + int64_t(vm) * kBM;
+    tile.row0 = lo + int64_t(vm) * C::BM;
     tile.row_end = hi;
     tile.bmat += int64_t(g) * args.b_group_stride;
     tile.bscale += int64_t(g) * args.bs_group_stride;
   } else {
-    tile.row0 = int64_t(tm) * kBM;
+    tile.row0 = int64_t(tm) * C::BM;
     tile.row_end = args.M;
   }
   return true;
 }
 
-// Global -> register staging of one K block: thread t holds 16-byte chunks
-// (rows (t/8) + 32p, bytes 16*(t%8)..) of the A and B tiles, plus one scale:
-// threads 0..127 the A scale of row t, threads 128.. the B scale(s).
-template <bool kRowScale>
-struct BlockLoad {
-  uint4 ra[4], rb[4];
-  float rs;
-
-  __device__ __forceinline__ void load(const GemmArgs& args, const Tile& tile, int kb) {
-    const int t = threadIdx.x;
-    const int cc = (t & 7) * 16;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = (t >> 3) + 32 * p;
-      const int64_t ar = tile.row0 + r;
-      ra[p] = ar < tile.row_end
-                  ? *reinterpret_cast<const uint4*>(args.a + ar * args.lda + int64_t(kb) * kBK + cc)
-                  : make_uint4(0, 0, 0, 0);
-      const int64_t br = tile.n0 + r;
-      rb[p] = br < args.N
-                  ? *reinterpret_cast<const uint4*>(tile.bmat + br * args.ldb + int64_t(kb) * kBK + cc)
-                  : make_uint4(0, 0, 0, 0);
-    }
-    rs = 0.0f;
-    if (t < kBM) {
-      const int64_t ar = tile.row0 + t;
-      if (ar < tile.row_end) rs = args.a_scale[ar * args.KB + kb];
-    } else if constexpr (kRowScale) {
-      const int64_t br = tile.n0 + (t - kBM);
-      if (br < args.N) rs = tile.bscale[br * args.KB + kb];
-    } else {
-      if (t == kBM) rs = tile.bscale[(tile.n0 / 128) * args.KB + kb];
-    }
+template <bool kBf16Out>
+__device__ __forceinline__ void store4(void* y, int64_t off, float v0, float v1, float v2, float v3) {
+  if constexpr (kBf16Out) {
+    const uint32_t lo = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
+    const uint32_t hi = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + off) = make_uint2(lo, hi);
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + off) = make_float4(v0, v1, v2, v3);
   }
-
-  __device__ __forceinline__ void store_scales(float* sA, float* sB) const {
-    const int t = threadIdx.x;
-    if (t < kBM) sA[t] = rs;
-    else if (kRowScale || t == kBM) sB[t - kBM] = rs;
-  }
-};
-
-// 16 E4M3 codes -> 16 f16 values (exact: every E4M3 value is an f16 value).
-__device__ __forceinline__ void widen16(const uint4& c, uint4& lo, uint4& hi) {
-  const h2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, false);
-  const h2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.x, 1.0f, true);
-  const h2 h2_ = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, false);
-  const h2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.y, 1.0f, true);
-  const h2 h4 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.z, 1.0f, false);
-  const h2 h5 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.z, 1.0f, true);
-  const h2 h6 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.w, 1.0f, false);
-  const h2 h7 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c.w, 1.0f, true);
-  lo = make_uint4(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
-                  __builtin_bit_cast(uint32_t, h2_), __builtin_bit_cast(uint32_t, h3));
-  hi = make_uint4(__builtin_bit_cast(uint32_t, h4), __builtin_bit_cast(uint32_t, h5),
-                  __builtin_bit_cast(uint32_t, h6), __builtin_bit_cast(uint32_t, h7));
 }
 
-template <bool kBf16Out>
-__device__ __forceinline__ void store_out(const GemmArgs& args, int64_t row, int64_t col, float v) {
-  if constexpr (kBf16Out)
-    reinterpret_cast<uint16_t*>(args.y)[row * args.ldy + col] = static_cast<uint16_t>(f32_to_bf16_rne(v));
-  else
-    reinterpret_cast<float*>(args.y)[row * args.ldy + col] = v;
+// 8 E4M3 codes (two words) -> 8 f16 values (exact).
+__device__ __forceinline__ h8 widen8(uint32_t w0, uint32_t w1) {
+  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return h8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // ---------------------------------------------------------------------------
-// FP32-accumulating kernel: f16 tiles in LDS, 32x32x16 f16 MFMA.
-// Each wave owns 2 x 2 sub-tiles of 32 x 32; lane l of a sub-tile holds
-// column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 for its 16 registers r.
-template <bool kRowScale, bool kBf16Out, bool kGrouped>
-__global__ __launch_bounds__(kThreads) void gemm_f32acc_kernel(const GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[2][kBM * kPitch16];
-  __shared__ __attribute__((aligned(16))) _Float16 Bs[2][kBN * kPitch16];
-  __shared__ __attribute__((aligned(16))) float sA[2][kBM];
-  __shared__ __attribute__((aligned(16))) float sB[2][kRowScale ? kBN : 4];
+template <class C, bool kF16, bool kRowScale, bool kBf16Out, bool kGrouped>
+__global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) {
+  using St = Stage<C::BM, C::BN, C::kWaves, kRowScale>;
+  __shared__ St st0, st1, st2;
+  constexpr int SM = C::SM, SN = C::SN, NW = C::kWaves;
 
   Tile tile;
-  if (!locate_tile<kGrouped>(args, tile)) return;
+  if (!locate_tile<C, kGrouped>(args, tile)) return;
   const int KB = args.KB;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % C::WM;
+  const int wn = wave / C::WM;
+  const int r32 = lane & 31;
+  const int hk = lane >> 5;
 
-  BlockLoad<kRowScale> ld;
-  auto stage = [&](int buf) {
-    const int cc = (t & 7) * 16;
+  const int64_t rows = min(tile.row_end - tile.row0, int64_t(C::BM));
+  const int64_t cols = min(int64_t(args.N) - tile.n0, int64_t(C::BN));
+  const i32x4 rs_a = make_rsrc(args.a + tile.row0 * args.lda, uint64_t(rows) * args.lda);
+  const i32x4 rs_b = make_rsrc(tile.bmat + tile.n0 * args.ldb, uint64_t(cols) * args.ldb);
+  const i32x4 rs_sa = make_rsrc(args.a_scale + tile.row0 * KB, uint64_t(rows) * KB * 4);
+  const i32x4 rs_sb = make_rsrc(tile.bscale + (kRowScale ? tile.n0 * KB : 0),
+                                kRowScale ? uint64_t(cols) * KB * 4 : 4);
+  // block128: this tile's row of B scales, read with scalar loads (the
+  // constant address space tells the compiler nothing writes it).
+  const __attribute__((address_space(4))) float* sb_blk =
+      (const __attribute__((address_space(4))) float*)(tile.bscale + (tile.n0 / 128) * KB);
+
+  // Per-lane source offsets of this wave's share of a stage (without the K
+  // block offset, which goes in the scalar offset).
+  constexpr int LA = C::BM / 8 / NW, LB = C::BN / 8 / NW;
+  constexpr int kLoadsPerStage = LA + LB + 1 + (kRowScale ? 1 : 0);   // per wave and stage
+  const int off_sa = (C::RSA * wave + lane % C::RSA) * KB * 4;
+  const int off_sb = (C::RSB * wave + lane % C::RSB) * KB * 4;
+  int off_a[LA], off_b[LB];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = (t >> 3) + 32 * p;
-      uint4 lo, hi;
-      widen16(ld.ra[p], lo, hi);
-      uint4* da = reinterpret_cast<uint4*>(&As[buf][r * kPitch16 + cc]);
-      da[0] = lo;
-      da[1] = hi;
-      widen16(ld.rb[p], lo, hi);
-      uint4* db = reinterpret_cast<uint4*>(&Bs[buf][r * kPitch16 + cc]);
-      db[0] = lo;
-      db[1] = hi;
-    }
-    ld.store_scales(sA[buf], sB[buf]);
+  for (int v = 0; v < LA; ++v) {
+    const int row = 8 * (v * NW + wave) + (lane >> 3);
+    off_a[v] = row * int(args.lda) + (((lane & 7) ^ swz(row)) << 4);
+  }
+#pragma unroll
+  for (int v = 0; v < LB; ++v) {
+    const int row = 8 * (v * NW + wave) + (lane >> 3);
+    off_b[v] = row * int(args.ldb) + (((lane & 7) ^ swz(row)) << 4);
+  }
+
+  auto load_stage = [&](St& s, int kb) {
+#pragma unroll
+    for (int v = 0; v < LA; ++v) dma16(rs_a, lds_addr(&s.a[(v * NW + wave) * 1024]), off_a[v], kb * 128);
+#pragma unroll
+    for (int v = 0; v < LB; ++v) dma16(rs_b, lds_addr(&s.b[(v * NW + wave) * 1024]), off_b[v], kb * 128);
+    dma4(rs_sa, lds_addr(&s.sa[wave][0]), off_sa, kb * 4);
+    if constexpr (kRowScale) dma4(rs_sb, lds_addr(&s.sb[wave][0]), off_sb, kb * 4);
   };
 
-  v16f acc[2][2];
+  v16f acc[SM][SN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < SM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < SN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  ld.load(args, tile, 0);
-  stage(0);
-  __syncthreads();
+  const int arow0 = wm * C::TM + r32;
+  const int brow0 = wn * C::TN + r32;
+  // LDS offsets of this lane's four 16-byte chunks (4 hk + q) of its first A
+  // and B rows; the rows 32 i further on have the same swizzle (it depends on
+  // row % 16 only), so they are these offsets plus 4096 i.
+  int a_off[4], b_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    a_off[q] = lds_off(arow0, 4 * hk + q);
+    b_off[q] = lds_off(brow0, 4 * hk + q);
+  }
 
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < KB) ld.load(args, tile, kb + 1);
-
-    v16f p[2][2];
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
-      h8 af[2], bf[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = *reinterpret_cast<const h8*>(&As[buf][(wm * 64 + mi * 32 + frow) * kPitch16 + s * 16 + fk]);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bf[ni] = *reinterpret_cast<const h8*>(&Bs[buf][(wn * 64 + ni * 32 + frow) * kPitch16 + s * 16 + fk]);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          if (s == 0) {
-            const v16f z = {};
-            p[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], z, 0, 0, 0);
-          } else {
-            p[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[mi], bf[ni], p[mi][ni], 0, 0, 0);
-          }
-        }
-    }
-
-    // Promotion: rows of register r are 8*(r/4) + 4*(lane/32) + r%4.
-    float sa[2][16];
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+  // One K block: block products P from the stage, then the promotion.
+  auto step = [&](const St& s, float sbv) {
+    v16f p[SM][SN];
+    if constexpr (kF16) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 s4 = *reinterpret_cast<const float4*>(&sA[buf][wm * 64 + mi * 32 + 8 * q + 4 * (lane >> 5)]);
-        sa[mi][4 * q + 0] = s4.x;
-        sa[mi][4 * q + 1] = s4.y;
-        sa[mi][4 * q + 2] = s4.z;
-        sa[mi][4 * q + 3] = s4.w;
-      }
-    if constexpr (!kRowScale) {
-      const float sb = sB[buf][0];
+        uint4 ra[SM], rb[SN];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+        for (int i = 0; i < SM; ++i) ra[i] = lds_read16(s.a, a_off[q] + 4096 * i);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sa[mi][r] *= sb;
-    }
-    float sbc[2] = {1.0f, 1.0f};
-    if constexpr (kRowScale) {
+        for (int j = 0; j < SN; ++j) rb[j] = lds_read16(s.b, b_off[q] + 4096 * j);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) sbc[ni] = sB[buf][wn * 64 + ni * 32 + frow];
-    }
+        for (int t = 0; t < 2; ++t) {
+          h8 fa[SM], fb[SN];
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
+          for (int i = 0; i < SM; ++i) fa[i] = t ? widen8(ra[i].z, ra[i].w) : widen8(ra[i].x, ra[i].y);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+          for (int j = 0; j < SN; ++j) fb[j] = t ? widen8(rb[j].z, rb[j].w) : widen8(rb[j].x, rb[j].y);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float c = kRowScale ? sa[mi][r] * sbc[ni] : sa[mi][r];
-          acc[mi][ni][r] = __builtin_fmaf(p[mi][ni][r], c, acc[mi][ni][r]);
+          for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int j = 0; j < SN; ++j) {
+              if (q == 0 && t == 0) {
+                const v16f z = {};
+                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], z, 0, 0, 0);
+              } else {
+                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], p[i][j], 0, 0, 0);
+              }
+            }
         }
-
-    if (kb + 1 < KB) stage(buf ^ 1);
-    __syncthreads();
-  }
-
+      }
+    } else {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+      for (int qq = 0; qq < 2; ++qq) {
+        v8i fa[SM], fb[SN];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t row = tile.row0 + wm * 64 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= tile.row_end) continue;
+        for (int i = 0; i < SM; ++i) {
+          const uint4 lo = lds_read16(s.a, a_off[2 * qq] + 4096 * i);
+          const uint4 hi = lds_read16(s.a, a_off[2 * qq + 1] + 4096 * i);
+          fa[i] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        }
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int64_t col = tile.n0 + wn * 64 + ni * 32 + frow;
-        if (col < args.N) store_out<kBf16Out>(args, row, col, acc[mi][ni][r]);
+        for (int j = 0; j < SN; ++j) {
+          const uint4 lo = lds_read16(s.b, b_off[2 * qq] + 4096 * j);
+          const uint4 hi = lds_read16(s.b, b_off[2 * qq + 1] + 4096 * j);
+          fb[j] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+        }
+#pragma unroll
+        for (int i = 0; i < SM; ++i)
+#pragma unroll
+          for (int j = 0; j < SN; ++j) {
+            // Format selectors 0/0 = E4M3 for both operands; zero scale
+            // operands give the plain (unscaled) instruction.
+            const v16f c = qq == 0 ? v16f{} : p[i][j];
+            p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], c, 0, 0, 0, 0, 0, 0);
+          }
       }
     }
-}
 
-// ---------------------------------------------------------------------------
-// FP8-MFMA kernel: E4M3 tiles in LDS (144-byte rows: 16 lanes reading 16
-// consecutive rows hit 16 distinct 4-bank groups), one 16x16x128 MFMA per
-// sub-tile and K block.  Each wave owns 4 x 4 sub-tiles of 16 x 16; lane l
-// holds column l%16 and rows 4*(l/16) + i.
-__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i& a, const v8i& b) {
-  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  // Format selectors 0/0 = E4M3 for both operands; zero scale operands make
-  // the compiler emit the plain (unscaled) v_mfma_f32_16x16x128_f8f6f4.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-template <bool kRowScale, bool kBf16Out, bool kGrouped>
-__global__ __launch_bounds__(kThreads) void gemm_fp8mfma_kernel(const GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][kBM * kPitch8];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBN * kPitch8];
-  __shared__ __attribute__((aligned(16))) float sA[2][kBM];
-  __shared__ __attribute__((aligned(16))) float sB[2][kRowScale ? kBN : 4];
-
-  Tile tile;
-  if (!locate_tile<kGrouped>(args, tile)) return;
-  const int KB = args.KB;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-
-  BlockLoad<kRowScale> ld;
-  auto stage = [&](int buf) {
-    const int cc = (t & 7) * 16;
+    // Promotion.  Accumulator r of subtile (i, j) is output row
+    // m = arow0 + 32 i and column n = wn*TN + 32 j + 8 (r/4) + 4 hk + r%4.
+    float ca[SM];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = (t >> 3) + 32 * p;
-      *reinterpret_cast<uint4*>(&As[buf][r * kPitch8 + cc]) = ld.ra[p];
-      *reinterpret_cast<uint4*>(&Bs[buf][r * kPitch8 + cc]) = ld.rb[p];
+    for (int i = 0; i < SM; ++i) {
+      const int m = arow0 + 32 * i;
+      ca[i] = s.sa[m / C::RSA][m % C::RSA];
     }
-    ld.store_scales(sA[buf], sB[buf]);
+    if constexpr (!kRowScale) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i) {
+        const float c = ca[i] * sbv;
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[i][j][r], c, acc[i][j][r]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = wn * C::TN + 32 * j + 8 * g + 4 * hk;
+          const float4 sb4 = *reinterpret_cast<const float4*>(&s.sb[n / C::RSB][n % C::RSB]);
+          const float sbr[4] = {sb4.x, sb4.y, sb4.z, sb4.w};
+#pragma unroll
+          for (int i = 0; i < SM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][4 * g + e] = __builtin_fmaf(p[i][j][4 * g + e], ca[i] * sbr[e], acc[i][j][4 * g + e]);
+        }
+    }
   };
 
-  float acc[4][4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[i][j][k] = 0.0f;
-
-  ld.load(args, tile, 0);
-  stage(0);
-  __syncthreads();
-
-  const int frag_row = lane & 15;
-  const int frag_k = (lane >> 4) * 32;
-  for (int kb = 0; kb < KB; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < KB) ld.load(args, tile, kb + 1);
-
-    v8i af[4], bf[4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const uint8_t* p = &As[buf][(wm * 64 + mi * 16 + frag_row) * kPitch8 + frag_k];
-      const uint4 lo = *reinterpret_cast<const uint4*>(p);
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-      af[mi] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const uint8_t* p = &Bs[buf][(wn * 64 + ni * 16 + frag_row) * kPitch8 + frag_k];
-      const uint4 lo = *reinterpret_cast<const uint4*>(p);
-      const uint4 hi = *reinterpret_cast<const uint4*>(p + 16);
-      bf[ni] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-    }
-    float sa[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      const float4 s4 = *reinterpret_cast<const float4*>(&sA[buf][wm * 64 + mi * 16 + 4 * (lane >> 4)]);
-      sa[mi][0] = s4.x; sa[mi][1] = s4.y; sa[mi][2] = s4.z; sa[mi][3] = s4.w;
-    }
-    if constexpr (!kRowScale) {
-      const float sb = sB[buf][0];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sa[mi][i] *= sb;
-    }
-    float sbc[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-    if constexpr (kRowScale) {
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) sbc[ni] = sB[buf][wn * 64 + ni * 16 + frag_row];
-    }
-
-    v4f p[4][4];
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) p[mi][ni] = mfma_fp8_16x16x128(af[mi], bf[ni]);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float c = kRowScale ? sa[mi][i] * sbc[ni] : sa[mi][i];
-          acc[mi][ni][i] = __builtin_fmaf(p[mi][ni][i], c, acc[mi][ni][i]);
-        }
-
-    if (kb + 1 < KB) stage(buf ^ 1);
-    __syncthreads();
+  // Prologue: K blocks 0 and 1 in flight.
+  load_stage(st0, 0);
+  if (KB > 1) {
+    load_stage(st1, 1);
+    wait_and_barrier<kLoadsPerStage>();
+  } else {
+    wait_and_barrier<0>();
   }
 
+  // Stage ring: block kb is in stage kb % 3; block kb + 2 is loaded while kb
+  // is multiplied; the barrier at the end of step kb makes block kb + 1
+  // visible and frees stage kb % 3 for block kb + 3.  The steady-state loop
+  // issues its loads unconditionally (three blocks per iteration, every one
+  // with kb + 2 < KB), which lets the compiler see that a read of the
+  // current stage does not wait for the loads just issued into another; the
+  // last (up to four) blocks run in a tail with the conditions spelled out.
+#define FP8BS_STEP_FULL(CUR, FUT, KBV)                                     \
+  {                                                                       \
+    const int kb_ = (KBV);                                                \
+    load_stage(FUT, kb_ + 2);                                             \
+    const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
+    step(CUR, sbv_);                                                      \
+    wait_and_barrier<kLoadsPerStage>();                                   \
+  }
+#define FP8BS_STEP_TAIL(CUR, FUT, KBV)                                     \
+  if ((KBV) < KB) {                                                       \
+    const int kb_ = (KBV);                                                \
+    if (kb_ + 2 < KB) load_stage(FUT, kb_ + 2);                           \
+    const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
+    step(CUR, sbv_);                                                      \
+    if (kb_ + 2 < KB) wait_and_barrier<kLoadsPerStage>();                 \
+    else if (kb_ + 1 < KB) wait_and_barrier<0>();                         \
+  }
+  int kb = 0;
+  for (; kb + 4 < KB; kb += 3) {
+    FP8BS_STEP_FULL(st0, st2, kb)
+    FP8BS_STEP_FULL(st1, st0, kb + 1)
+    FP8BS_STEP_FULL(st2, st1, kb + 2)
+  }
+  FP8BS_STEP_TAIL(st0, st2, kb)
+  FP8BS_STEP_TAIL(st1, st0, kb + 1)
+  FP8BS_STEP_TAIL(st2, st1, kb + 2)
+  FP8BS_STEP_TAIL(st0, st2, kb + 3)
+#undef FP8BS_STEP_FULL
+#undef FP8BS_STEP_TAIL
+
+  // Epilogue: four consecutive columns per store.
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int i = 0; i < SM; ++i) {
+    const int64_t row = tile.row0 + arow0 + 32 * i;
+    if (row >= tile.row_end) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = tile.row0 + wm * 64 + mi * 16 + 4 * (lane >> 4) + i;
-      if (row >= tile.row_end) continue;
+    for (int j = 0; j < SN; ++j)
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const int64_t col = tile.n0 + wn * 64 + ni * 16 + frag_row;
-        if (col < args.N) store_out<kBf16Out>(args, row, col, acc[mi][ni][i]);
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = tile.n0 + wn * C::TN + 32 * j + 8 * g + 4 * hk;
+        if (col < args.N)
+          store4<kBf16Out>(args.y, row * args.ldy + col, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                           acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-#define FP8BS_DEFINE_LAUNCH(NAME)                                                                   \
-  template <bool kGrouped>                                                                         \
-  void launch_##NAME(const GemmArgs& args, bool row_scale, bool bf16_out, uint32_t n_wg,           \
-                     hipStream_t stream) {                                                         \
-    const dim3 grid(n_wg), block(kThreads);                                                        \
-    if (row_scale) {                                                                               \
-      if (bf16_out)                                                                                \
-        hipLaunchKernelGGL((NAME<true, true, kGrouped>), grid, block, 0, stream, args);            \
-      else                                                                                         \
-        hipLaunchKernelGGL((NAME<true, false, kGrouped>), grid, block, 0, stream, args);           \
-    } else {                                                                                       \
-      if (bf16_out)                                                                                \
-        hipLaunchKernelGGL((NAME<false, true, kGrouped>), grid, block, 0, stream, args);           \
-      else                                                                                         \
-        hipLaunchKernelGGL((NAME<false, false, kGrouped>), grid, block, 0, stream, args);          \
-    }                                                                                              \
+using CfgLarge = TileCfg<256, 128, 4, 2>;   // 256 x 128 tile, 8 waves of 64 x 64
+using CfgSmall = TileCfg<128, 128, 2, 2>;   // 128 x 128 tile, 4 waves of 64 x 64
+
+template <class C, bool kGrouped>
+void launch_cfg(const GemmArgs& args, bool f16, bool row_scale, bool bf16_out, uint32_t n_wg,
+                hipStream_t stream) {
+  const dim3 grid(n_wg), block(C::kThreads);
+#define FP8BS_L(F, R, B) hipLaunchKernelGGL((gemm_kernel<C, F, R, B, kGrouped>), grid, block, 0, stream, args)
+  if (f16) {
+    if (row_scale) { if (bf16_out) FP8BS_L(true, true, true); else FP8BS_L(true, true, false); }
+    else { if (bf16_out) FP8BS_L(true, false, true); else FP8BS_L(true, false, false); }
+  } else {
+    if (row_scale) { if (bf16_out) FP8BS_L(false, true, true); else FP8BS_L(false, true, false); }
+    else { if (bf16_out) FP8BS_L(false, false, true); else FP8BS_L(false, false, false); }
   }
-
-FP8BS_DEFINE_LAUNCH(gemm_f32acc_kernel)
-FP8BS_DEFINE_LAUNCH(gemm_fp8mfma_kernel)
-#undef FP8BS_DEFINE_LAUNCH
-
-template <bool kGrouped>
-fp8bs_status launch(const GemmArgs& args, int32_t accum, bool row_scale, bool bf16_out,
-                    uint32_t n_wg, hipStream_t stream) {
-  if (accum == FP8BS_ACCUM_FP8_MFMA)
-    launch_gemm_fp8mfma_kernel<kGrouped>(args, row_scale, bf16_out, n_wg, stream);
-  else
-    launch_gemm_f32acc_kernel<kGrouped>(args, row_scale, bf16_out, n_wg, stream);
-  return check_launch(kGrouped ? "fp8_blockscaled_grouped_gemm" : "fp8_blockscaled_gemm");
+#undef FP8BS_L
 }
+
+// Tile size: the large tile when it still gives at least one workgroup per
+// CU, otherwise the small one.
+constexpr int64_t kNumCU = 256;
 
 bool valid_accum(int32_t accum) { return accum == FP8BS_ACCUM_FP32 || accum == FP8BS_ACCUM_FP8_MFMA; }
 
@@ -518,21 +519,35 @@ extern "C" fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, co
       (ldy * elem_size(y_dtype)) % 16)
     return fail(FP8BS_ERR_ALIGNMENT, "%s: operands and row pitches must be 16-byte aligned", fn);
   if (!aligned4(a_scale) || !aligned4(b_scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
-  if (M > 0x7fffffff || N > 0x7fffffff || K / 128 > 0x7fffffff)
+  if (M > 0x7fffffff || N > 0x7fffffff)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: dimension too large", fn);
+  // Offsets inside one tile are 32-bit: 256 rows of codes or scales.
+  if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || K / 128 * 256 * 4 > 0x7fffffff)
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: row pitch too large", fn);
 
   GemmArgs args{};
   args.a = a; args.a_scale = a_scale; args.b = b; args.b_scale = b_scale; args.y = y;
   args.off = nullptr;
   args.lda = lda; args.ldb = ldb; args.ldy = ldy;
   args.M = int32_t(M); args.N = int32_t(N); args.KB = int32_t(K / 128);
-  args.tiles_m = int32_t((M + kBM - 1) / kBM);
-  args.tiles_n = int32_t((N + kBN - 1) / kBN);
   args.G = 1;
-  const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-  if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-  return launch<false>(args, accum, b_kind == FP8BS_BSCALE_ROW, y_dtype == FP8BS_BF16,
-                       uint32_t(n_wg), stream);
+  const bool f16 = accum == FP8BS_ACCUM_FP32;
+  const bool row = b_kind == FP8BS_BSCALE_ROW;
+  const bool bf16 = y_dtype == FP8BS_BF16;
+  const int64_t tiles_large = ((M + 255) / 256) * ((N + 127) / 128);
+  if (tiles_large >= kNumCU) {
+    args.tiles_m = int32_t((M + 255) / 256);
+    args.tiles_n = int32_t((N + 127) / 128);
+    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
+    launch_cfg<CfgLarge, false>(args, f16, row, bf16, uint32_t(n_wg), stream);
+  } else {
+    args.tiles_m = int32_t((M + 127) / 128);
+    args.tiles_n = int32_t((N + 127) / 128);
+    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+    launch_cfg<CfgSmall, false>(args, f16, row, bf16, uint32_t(n_wg), stream);
+  }
+  return check_launch(fn);
 }
 
 extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t G,
@@ -553,7 +568,8 @@ extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N,
     return fail(FP8BS_ERR_ALIGNMENT, "%s: operands must be 16-byte aligned", fn);
   if (!aligned4(a_scale) || !aligned4(b_scale) || !aligned4(off))
     return fail(FP8BS_ERR_ALIGNMENT, "%s: scales and offsets must be 4-byte aligned", fn);
-  if (M_total > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: M_total too large", fn);
+  if (M_total > 0x7fffffff || N > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: size too large", fn);
+  if (K > (int64_t(1) << 22)) return fail(FP8BS_ERR_INVALID_ARG, "%s: K too large", fn);
 
   GemmArgs args{};
   args.a = a; args.a_scale = a_scale; args.b = b; args.b_scale = b_scale; args.y = y;
@@ -562,10 +578,23 @@ extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N,
   args.b_group_stride = N * K;
   args.bs_group_stride = (N / 128) * (K / 128);
   args.M = int32_t(M_total); args.N = int32_t(N); args.KB = int32_t(K / 128);
-  args.tiles_m = int32_t((M_total + kBM - 1) / kBM + G);   // upper bound on sum_g ceil(m_g/128)
-  args.tiles_n = int32_t(N / kBN);
   args.G = G;
-  const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-  if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-  return launch<true>(args, accum, false, y_dtype == FP8BS_BF16, uint32_t(n_wg), stream);
+  const bool f16 = accum == FP8BS_ACCUM_FP32;
+  const bool bf16 = y_dtype == FP8BS_BF16;
+  // Upper bound on sum_g ceil(m_g / BM): ceil(M_total / BM) + G.
+  const int64_t tiles_large = ((M_total + 255) / 256 + G) * (N / 128);
+  if (tiles_large >= 2 * kNumCU) {
+    args.tiles_m = int32_t((M_total + 255) / 256 + G);
+    args.tiles_n = int32_t(N / 128);
+    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
+    launch_cfg<CfgLarge, true>(args, f16, false, bf16, uint32_t(n_wg), stream);
+  } else {
+    args.tiles_m = int32_t((M_total + 127) / 128 + G);
+    args.tiles_n = int32_t(N / 128);
+    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
+    launch_cfg<CfgSmall, true>(args, f16, false, bf16, uint32_t(n_wg), stream);
+  }
+  return check_launch(fn);
 }
