@@ -51,6 +51,10 @@
 #include "fp8bs.h"
 #include "status.hpp"
 
+#ifndef FP8BS_LAG
+#define FP8BS_LAG 0
+#endif
+
 namespace fp8bs {
 
 namespace {
@@ -129,20 +133,25 @@ struct TileCfg {
   static constexpr int kGroupM = 4;                 // tile-walk group height (M tiles)
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 subtiles");
   static_assert((BM / 8) % kWaves == 0 && (BN / 8) % kWaves == 0, "tile loads must split evenly");
-  static constexpr int RSA = BM / kWaves, RSB = BN / kWaves;   // scale rows per wave
-  static_assert(RSA <= 64 && 64 % RSA == 0 && RSB <= 64 && 64 % RSB == 0, "scale rows per wave");
+  // Scale loads: one 64-lane load covers 16 rows x 4 K blocks.
+  static constexpr int kScaleLoadsA = BM / 16 / kWaves, kScaleLoadsB = BN / 16 / kWaves;
+  static_assert((BM / 16) % kWaves == 0 && (BN / 16) % kWaves == 0, "scale loads must split evenly");
 };
 
-// One K block of the A and B tiles and their scales.  Every wave loads the
-// scales of BM / waves rows (and BN / waves per-row B scales) with one 64-lane
-// load into its own 64-float slot, lane i taking row (i % rows-per-wave), so
-// each wave issues the same number of loads per stage.
-template <int BM, int BN, int NW, bool kRowScale>
+// One K block of the A and B tiles.
+template <int BM, int BN>
 struct alignas(16) Stage {
   uint8_t a[BM * 128];
   uint8_t b[BN * 128];
-  float sa[NW][64];
-  float sb[kRowScale ? NW : 1][64];
+};
+
+// Scales of four consecutive K blocks: [row][kb % 4].  A 64-lane load fills
+// 16 rows x 4 blocks (16 cache lines), where loading one block per step would
+// touch one line per row.  Two of these alternate.
+template <int BM, int BN, bool kRowScale>
+struct alignas(16) ScaleGroup {
+  float sa[BM][4];
+  float sb[kRowScale ? BN : 1][4];
 };
 
 // 16-byte chunk swizzle of a 128-byte LDS row.
@@ -238,8 +247,10 @@ __device__ __forceinline__ h8 widen8(uint32_t w0, uint32_t w1) {
 // ---------------------------------------------------------------------------
 template <class C, bool kF16, bool kRowScale, bool kBf16Out, bool kGrouped>
 __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) {
-  using St = Stage<C::BM, C::BN, C::kWaves, kRowScale>;
+  using St = Stage<C::BM, C::BN>;
+  using Sg = ScaleGroup<C::BM, C::BN, kRowScale>;
   __shared__ St st0, st1, st2;
+  __shared__ Sg sg[2];
   constexpr int SM = C::SM, SN = C::SN, NW = C::kWaves;
 
   Tile tile;
@@ -264,31 +275,42 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
   const __attribute__((address_space(4))) float* sb_blk =
       (const __attribute__((address_space(4))) float*)(tile.bscale + (tile.n0 / 128) * KB);
 
-  // Per-lane source offsets of this wave's share of a stage (without the K
-  // block offset, which goes in the scalar offset).
+  // Per-lane source offsets of this wave's share of a stage.  Load v of the
+  // wave covers rows 8 (v * NW + wave) .. + 7, lane i taking row + i / 8 and
+  // the logical chunk that lands at physical chunk i % 8.  The swizzle of
+  // those rows does not depend on v (NW is even), so one VGPR offset per
+  // operand serves every v; the row-group term and the K block offset go in
+  // the scalar offset.
   constexpr int LA = C::BM / 8 / NW, LB = C::BN / 8 / NW;
-  constexpr int kLoadsPerStage = LA + LB + 1 + (kRowScale ? 1 : 0);   // per wave and stage
-  const int off_sa = (C::RSA * wave + lane % C::RSA) * KB * 4;
-  const int off_sb = (C::RSB * wave + lane % C::RSB) * KB * 4;
-  int off_a[LA], off_b[LB];
-#pragma unroll
-  for (int v = 0; v < LA; ++v) {
-    const int row = 8 * (v * NW + wave) + (lane >> 3);
-    off_a[v] = row * int(args.lda) + (((lane & 7) ^ swz(row)) << 4);
-  }
-#pragma unroll
-  for (int v = 0; v < LB; ++v) {
-    const int row = 8 * (v * NW + wave) + (lane >> 3);
-    off_b[v] = row * int(args.ldb) + (((lane & 7) ^ swz(row)) << 4);
-  }
+  constexpr int kLoadsPerStage = LA + LB;   // tile loads per wave and stage
+  static_assert(NW % 2 == 0, "the swizzle argument needs an even wave count");
+  const int lrow = 8 * wave + (lane >> 3);
+  const int chunk = ((lane & 7) ^ swz(lrow)) << 4;
+  const int voff_a = lrow * int(args.lda) + chunk;
+  const int voff_b = lrow * int(args.ldb) + chunk;
+  // Scale-group loads: load u of this wave covers rows 16 (u * NW + wave) +
+  // lane / 4 and K block 4 g + lane % 4.
+  const int voff_s = ((16 * wave + (lane >> 2)) * KB + (lane & 3)) * 4;
 
   auto load_stage = [&](St& s, int kb) {
 #pragma unroll
-    for (int v = 0; v < LA; ++v) dma16(rs_a, lds_addr(&s.a[(v * NW + wave) * 1024]), off_a[v], kb * 128);
+    for (int v = 0; v < LA; ++v)
+      dma16(rs_a, lds_addr(&s.a[(v * NW + wave) * 1024]), voff_a, kb * 128 + 8 * v * NW * int(args.lda));
 #pragma unroll
-    for (int v = 0; v < LB; ++v) dma16(rs_b, lds_addr(&s.b[(v * NW + wave) * 1024]), off_b[v], kb * 128);
-    dma4(rs_sa, lds_addr(&s.sa[wave][0]), off_sa, kb * 4);
-    if constexpr (kRowScale) dma4(rs_sb, lds_addr(&s.sb[wave][0]), off_sb, kb * 4);
+    for (int v = 0; v < LB; ++v)
+      dma16(rs_b, lds_addr(&s.b[(v * NW + wave) * 1024]), voff_b, kb * 128 + 8 * v * NW * int(args.ldb));
+  };
+  // Scales of K blocks 4 g .. 4 g + 3 into sg[g & 1].
+  auto load_scales = [&](int g) {
+    Sg& d = sg[g & 1];
+#pragma unroll
+    for (int u = 0; u < C::kScaleLoadsA; ++u)
+      dma4(rs_sa, lds_addr(&d.sa[16 * (u * NW + wave)][0]), voff_s, g * 16 + 16 * u * NW * KB * 4);
+    if constexpr (kRowScale) {
+#pragma unroll
+      for (int u = 0; u < C::kScaleLoadsB; ++u)
+        dma4(rs_sb, lds_addr(&d.sb[16 * (u * NW + wave)][0]), voff_s, g * 16 + 16 * u * NW * KB * 4);
+    }
   };
 
   v16f acc[SM][SN];
@@ -311,100 +333,174 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
     b_off[q] = lds_off(brow0, 4 * hk + q);
   }
 
-  // One K block: block products P from the stage, then the promotion.
-  auto step = [&](const St& s, float sbv) {
-    v16f p[SM][SN];
-    if constexpr (kF16) {
+  // Block partials.  With the block-128 B scales the promotion is lagged by
+  // one K block: the partials of block kb stay in p and are promoted at the
+  // start of step kb + 1, subtile by subtile just before that subtile's first
+  // matrix instruction, so the FMAs issue while the matrix core works on the
+  // other subtiles.  cprev holds their per-row factors sa * sb.
+  constexpr bool kLag = !kRowScale && FP8BS_LAG;
+  v16f p[SM][SN];
+  float cprev[SM];
+  if constexpr (kLag) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint4 ra[SM], rb[SN];
+    for (int i = 0; i < SM; ++i) {
+      cprev[i] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < SM; ++i) ra[i] = lds_read16(s.a, a_off[q] + 4096 * i);
+      for (int j = 0; j < SN; ++j)
 #pragma unroll
-        for (int j = 0; j < SN; ++j) rb[j] = lds_read16(s.b, b_off[q] + 4096 * j);
+        for (int r = 0; r < 16; ++r) p[i][j][r] = 0.0f;
+    }
+  }
+  auto promote = [&](int i, int j, float c) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          h8 fa[SM], fb[SN];
+    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[i][j][r], c, acc[i][j][r]);
+  };
+
+  // Operand fragments, carried across steps.  f16 path: raw E4M3 slices of
+  // 16 bytes per row (two 16-deep k-steps), slice q in buffer q & 1.  FP8
+  // path: 32-byte slices (one 64-deep matrix instruction), slice qq in
+  // buffer qq.  Slice 0 of the next block is read into buffer 0 right after
+  // the barrier that makes that block visible, while the current block's
+  // last slice is multiplied.
+  uint4 ra[2][SM], rb[2][SN];
+  v8i fa8[2][SM], fb8[2][SN];
+  auto read_slice = [&](const St& s, int q, int buf) {
 #pragma unroll
-          for (int i = 0; i < SM; ++i) fa[i] = t ? widen8(ra[i].z, ra[i].w) : widen8(ra[i].x, ra[i].y);
+    for (int i = 0; i < SM; ++i) ra[buf][i] = lds_read16(s.a, a_off[q] + 4096 * i);
 #pragma unroll
-          for (int j = 0; j < SN; ++j) fb[j] = t ? widen8(rb[j].z, rb[j].w) : widen8(rb[j].x, rb[j].y);
+    for (int j = 0; j < SN; ++j) rb[buf][j] = lds_read16(s.b, b_off[q] + 4096 * j);
+  };
+  auto read_slice8 = [&](const St& s, int qq, int buf) {
 #pragma unroll
-          for (int i = 0; i < SM; ++i)
+    for (int i = 0; i < SM; ++i) {
+      const uint4 lo = lds_read16(s.a, a_off[2 * qq] + 4096 * i);
+      const uint4 hi = lds_read16(s.a, a_off[2 * qq + 1] + 4096 * i);
+      fa8[buf][i] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    }
 #pragma unroll
-            for (int j = 0; j < SN; ++j) {
-              if (q == 0 && t == 0) {
-                const v16f z = {};
-                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], z, 0, 0, 0);
-              } else {
-                p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], p[i][j], 0, 0, 0);
-              }
-            }
-        }
-      }
-    } else {
+    for (int j = 0; j < SN; ++j) {
+      const uint4 lo = lds_read16(s.b, b_off[2 * qq] + 4096 * j);
+      const uint4 hi = lds_read16(s.b, b_off[2 * qq + 1] + 4096 * j);
+      fb8[buf][j] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
+    }
+  };
+  // f16 path: widen slice q and run its two k-steps.
+  auto mma_slice = [&](int q, int buf) {
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) {
-        v8i fa[SM], fb[SN];
+    for (int t = 0; t < 2; ++t) {
+      h8 fa[SM], fb[SN];
 #pragma unroll
-        for (int i = 0; i < SM; ++i) {
-          const uint4 lo = lds_read16(s.a, a_off[2 * qq] + 4096 * i);
-          const uint4 hi = lds_read16(s.a, a_off[2 * qq + 1] + 4096 * i);
-          fa[i] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-        }
+      for (int i = 0; i < SM; ++i)
+        fa[i] = t ? widen8(ra[buf][i].z, ra[buf][i].w) : widen8(ra[buf][i].x, ra[buf][i].y);
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+        fb[j] = t ? widen8(rb[buf][j].z, rb[buf][j].w) : widen8(rb[buf][j].x, rb[buf][j].y);
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
-          const uint4 lo = lds_read16(s.b, b_off[2 * qq] + 4096 * j);
-          const uint4 hi = lds_read16(s.b, b_off[2 * qq + 1] + 4096 * j);
-          fb[j] = v8i{int(lo.x), int(lo.y), int(lo.z), int(lo.w), int(hi.x), int(hi.y), int(hi.z), int(hi.w)};
-        }
-#pragma unroll
-        for (int i = 0; i < SM; ++i)
-#pragma unroll
-          for (int j = 0; j < SN; ++j) {
-            // Format selectors 0/0 = E4M3 for both operands; zero scale
-            // operands give the plain (unscaled) instruction.
-            const v16f c = qq == 0 ? v16f{} : p[i][j];
-            p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[j], fa[i], c, 0, 0, 0, 0, 0, 0);
+          if (q == 0 && t == 0) {
+            // Promote the previous block's partial of this subtile, then
+            // start the new one in the same registers; the fences keep the
+            // compiler from overlapping the two (which would need 16 more
+            // registers per subtile).
+            if constexpr (kLag) {
+              promote(i, j, cprev[i]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            const v16f z = {};
+            p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], z, 0, 0, 0);
+            if constexpr (kLag) __builtin_amdgcn_sched_barrier(0);
+          } else {
+            p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], p[i][j], 0, 0, 0);
           }
-      }
+        }
     }
+  };
+  // FP8 path: one 64-deep instruction per subtile.  Format selectors 0/0 =
+  // E4M3 for both operands; zero scale operands give the plain instruction.
+  auto mma_slice8 = [&](int qq) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        if (qq == 0) {
+          if constexpr (kLag) {
+            promote(i, j, cprev[i]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[0][j], fa8[0][i], v16f{}, 0, 0, 0, 0, 0, 0);
+          if constexpr (kLag) __builtin_amdgcn_sched_barrier(0);
+        } else {
+          p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[1][j], fa8[1][i], p[i][j], 0, 0, 0, 0, 0, 0);
+        }
+      }
+  };
+
+  // One K block from stage s.  mode 0: last block; 1: the next block's
+  // loads are complete except those of the block after it (issued at the
+  // start of this step); 2: the next block's loads are the last ones.  Every
+  // read of stage s is issued before the barrier, which is what lets the
+  // next step refill it.  The scales are read after it: their group buffer
+  // is refilled only two steps later.
+  auto step = [&](const St& s, const St& nxt, int kb, float sbv, int mode) {
+    const Sg& scl = sg[(kb >> 2) & 1];
+    // The scheduling fences keep the compiler from hoisting later slices'
+    // reads and widening ahead of the current slice's matrix work, which
+    // would raise register pressure past the two-waves-per-SIMD budget.
+    if constexpr (kF16) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        read_slice(s, q + 1, (q + 1) & 1);
+        mma_slice(q, q & 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      read_slice8(s, 1, 1);
+      mma_slice8(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (mode == 1) wait_and_barrier<kLoadsPerStage>();
+    else if (mode == 2) wait_and_barrier<0>();
+    if (mode != 0) {
+      if constexpr (kF16) read_slice(nxt, 0, 0);
+      else read_slice8(nxt, 0, 0);
+    }
+    if constexpr (kF16) mma_slice(3, 1);
+    else mma_slice8(1);
+    __builtin_amdgcn_sched_barrier(0);
 
     // Promotion.  Accumulator r of subtile (i, j) is output row
     // m = arow0 + 32 i and column n = wn*TN + 32 j + 8 (r/4) + 4 hk + r%4.
     float ca[SM];
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int m = arow0 + 32 * i;
-      ca[i] = s.sa[m / C::RSA][m % C::RSA];
-    }
-    if constexpr (!kRowScale) {
+    for (int i = 0; i < SM; ++i) ca[i] = scl.sa[arow0 + 32 * i][kb & 3];
+    if constexpr (kLag) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i) cprev[i] = ca[i] * sbv;
+    } else if constexpr (!kRowScale) {
 #pragma unroll
       for (int i = 0; i < SM; ++i) {
         const float c = ca[i] * sbv;
 #pragma unroll
-        for (int j = 0; j < SN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[i][j][r], c, acc[i][j][r]);
+        for (int j = 0; j < SN; ++j) promote(i, j, c);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < SN; ++j)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = wn * C::TN + 32 * j + 8 * g + 4 * hk;
-          const float4 sb4 = *reinterpret_cast<const float4*>(&s.sb[n / C::RSB][n % C::RSB]);
-          const float sbr[4] = {sb4.x, sb4.y, sb4.z, sb4.w};
+        for (int r = 0; r < 16; ++r) {
+          const float sbn = scl.sb[wn * C::TN + 32 * j + 8 * (r >> 2) + 4 * hk + (r & 3)][kb & 3];
 #pragma unroll
           for (int i = 0; i < SM; ++i)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              acc[i][j][4 * g + e] = __builtin_fmaf(p[i][j][4 * g + e], ca[i] * sbr[e], acc[i][j][4 * g + e]);
+            acc[i][j][r] = __builtin_fmaf(p[i][j][r], ca[i] * sbn, acc[i][j][r]);
         }
     }
   };
 
-  // Prologue: K blocks 0 and 1 in flight.
+  // Prologue: scales of K blocks 0..3 and K blocks 0 and 1 in flight,
+  // block 0 visible, its slice 0 read.
+  load_scales(0);
   load_stage(st0, 0);
   if (KB > 1) {
     load_stage(st1, 1);
@@ -412,43 +508,55 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
   } else {
     wait_and_barrier<0>();
   }
+  if constexpr (kF16) read_slice(st0, 0, 0);
+  else read_slice8(st0, 0, 0);
 
   // Stage ring: block kb is in stage kb % 3; block kb + 2 is loaded while kb
-  // is multiplied; the barrier at the end of step kb makes block kb + 1
-  // visible and frees stage kb % 3 for block kb + 3.  The steady-state loop
-  // issues its loads unconditionally (three blocks per iteration, every one
-  // with kb + 2 < KB), which lets the compiler see that a read of the
-  // current stage does not wait for the loads just issued into another; the
-  // last (up to four) blocks run in a tail with the conditions spelled out.
-#define FP8BS_STEP_FULL(CUR, FUT, KBV)                                     \
+  // is multiplied; the barrier inside step kb makes block kb + 1 visible and,
+  // since every read of stage kb % 3 precedes it, lets step kb + 1 refill
+  // that stage with block kb + 3.  The steady-state loop issues its loads
+  // unconditionally (three blocks per iteration, every one with kb + 2 < KB);
+  // the last (up to four) blocks run in a tail with the conditions spelled
+  // out.  Scale group g + 1 (blocks 4 g + 4 ..) is loaded at step 4 g + 1,
+  // ahead of that step's tile loads, so the barrier inside step 4 g + 1
+  // already covers it; its buffer held group g - 1, last read in step
+  // 4 g - 1, which every wave has finished once it passes the barrier of
+  // step 4 g.
+#define FP8BS_STEP_FULL(CUR, NXT, FUT, KBV)                                \
   {                                                                       \
     const int kb_ = (KBV);                                                \
+    if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     load_stage(FUT, kb_ + 2);                                             \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(CUR, sbv_);                                                      \
-    wait_and_barrier<kLoadsPerStage>();                                   \
+    step(CUR, NXT, kb_, sbv_, 1);                                         \
   }
-#define FP8BS_STEP_TAIL(CUR, FUT, KBV)                                     \
+#define FP8BS_STEP_TAIL(CUR, NXT, FUT, KBV)                                \
   if ((KBV) < KB) {                                                       \
     const int kb_ = (KBV);                                                \
+    if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     if (kb_ + 2 < KB) load_stage(FUT, kb_ + 2);                           \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(CUR, sbv_);                                                      \
-    if (kb_ + 2 < KB) wait_and_barrier<kLoadsPerStage>();                 \
-    else if (kb_ + 1 < KB) wait_and_barrier<0>();                         \
+    step(CUR, NXT, kb_, sbv_, kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2)); \
   }
   int kb = 0;
   for (; kb + 4 < KB; kb += 3) {
-    FP8BS_STEP_FULL(st0, st2, kb)
-    FP8BS_STEP_FULL(st1, st0, kb + 1)
-    FP8BS_STEP_FULL(st2, st1, kb + 2)
+    FP8BS_STEP_FULL(st0, st1, st2, kb)
+    FP8BS_STEP_FULL(st1, st2, st0, kb + 1)
+    FP8BS_STEP_FULL(st2, st0, st1, kb + 2)
   }
-  FP8BS_STEP_TAIL(st0, st2, kb)
-  FP8BS_STEP_TAIL(st1, st0, kb + 1)
-  FP8BS_STEP_TAIL(st2, st1, kb + 2)
-  FP8BS_STEP_TAIL(st0, st2, kb + 3)
+  FP8BS_STEP_TAIL(st0, st1, st2, kb)
+  FP8BS_STEP_TAIL(st1, st2, st0, kb + 1)
+  FP8BS_STEP_TAIL(st2, st0, st1, kb + 2)
+  FP8BS_STEP_TAIL(st0, st1, st2, kb + 3)
 #undef FP8BS_STEP_FULL
 #undef FP8BS_STEP_TAIL
+
+  if constexpr (kLag) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) promote(i, j, cprev[i]);
+  }
 
   // Epilogue: four consecutive columns per store.
 #pragma unroll
