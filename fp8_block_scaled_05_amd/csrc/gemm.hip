@@ -629,6 +629,8 @@ extern "C" fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, co
   if (!aligned4(a_scale) || !aligned4(b_scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
   if (M > 0x7fffffff || N > 0x7fffffff)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: dimension too large", fn);
+  if (!sane_matrix(M, ldy, elem_size(y_dtype)) || !sane_matrix(M, lda, 1) || !sane_matrix(N, ldb, 1))
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: sizes and pitches exceed any allocation", fn);
   // Offsets inside one tile are 32-bit: 256 rows of codes or scales.
   if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || K / 128 * 256 * 4 > 0x7fffffff)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: row pitch too large", fn);
@@ -677,6 +679,9 @@ extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N,
   if (!aligned4(a_scale) || !aligned4(b_scale) || !aligned4(off))
     return fail(FP8BS_ERR_ALIGNMENT, "%s: scales and offsets must be 4-byte aligned", fn);
   if (M_total > 0x7fffffff || N > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: size too large", fn);
+  if (!sane_matrix(M_total, N, elem_size(y_dtype)) || !sane_matrix(M_total, K, 1) ||
+      !sane_matrix(int64_t(G) * N, K, 1))
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: sizes exceed any allocation", fn);
   if (K > (int64_t(1) << 22)) return fail(FP8BS_ERR_INVALID_ARG, "%s: K too large", fn);
 
   GemmArgs args{};

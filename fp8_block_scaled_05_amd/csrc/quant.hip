@@ -73,7 +73,24 @@ __device__ __forceinline__ float absmax8(const float (&v)[8]) {
 // handles 4 consecutive tiles per step and kU steps, all loads issued before
 // the first use.  Tile t is row t / KB, column block t % KB, and its scale
 // sits at scale[t] (the scale array is dense [rows, KB]).
-constexpr int kActU = 4;
+#ifndef FP8BS_ACT_U
+#define FP8BS_ACT_U 2
+#endif
+#ifndef FP8BS_NT_STORE
+#define FP8BS_NT_STORE 1
+#endif
+constexpr int kActU = FP8BS_ACT_U;
+
+// Code stores cover whole cache lines per wave and are not read again here,
+// so they stream past the caches (nontemporal).  Scale stores are 16 bytes
+// per wave and step; they stay ordinary stores so that L2 merges them into
+// whole lines before they reach memory.
+__device__ __forceinline__ void store_codes8(uint8_t* dst, uint2 c) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  if (FP8BS_NT_STORE) __builtin_nontemporal_store(u32x2{c.x, c.y}, reinterpret_cast<u32x2*>(dst));
+  else *reinterpret_cast<uint2*>(dst) = c;
+}
+__device__ __forceinline__ void store_scale(float* dst, float s) { *dst = s; }
 
 template <bool kBf16, int kU>
 __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict__ x, int64_t ld_x,
@@ -108,8 +125,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
     const uint2 codes = encode8<kBf16>(v[u], s, r);
     if (tile[u] < n_tiles) {
       uint8_t* dst = q + int64_t(row[u]) * ld_q + int64_t(kb[u]) * 128 + sub * 8;
-      *reinterpret_cast<uint2*>(dst) = codes;
-      if (sub == 0) scale[tile[u]] = s;
+      store_codes8(dst, codes);
+      if (sub == 0) store_scale(&scale[tile[u]], s);
     }
   }
 }
@@ -217,13 +234,20 @@ __global__ __launch_bounds__(256) void quant_128x1_t_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 blocks.  One workgroup per block: thread t holds rows
-// (t/16) + 16p (p < 8), columns 8*(t%16)..+8, i.e. 64 values in registers.
-// Block amax: per-thread max, wave max, then the 4 waves through LDS.  With
-// the transposed copy requested, the codes go through LDS (row pitch 132
-// bytes) and each thread transposes one 8x8 byte sub-block with byte
-// permutes, writing 8-byte pieces of the transposed rows.
+// 128x128 blocks.  One workgroup of kThreads threads per block: thread t
+// holds columns 8*(t%16)..+8 of rows t/16 + (kThreads/16) p, i.e.
+// 2048/kThreads rows of 8 values in registers.  Block amax: per-thread max,
+// wave max, then the waves through LDS.  With the transposed copy requested,
+// the codes go through LDS (row pitch 132 bytes) and each of the first 256
+// threads transposes one 8x8 byte sub-block with byte permutes, writing
+// 8-byte pieces of the transposed rows.
 constexpr int kCPitch = 132;  // bytes
+#ifndef FP8BS_W_THREADS
+#define FP8BS_W_THREADS 512
+#endif
+#ifndef FP8BS_W_GRID
+#define FP8BS_W_GRID 65536
+#endif
 
 __device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
                                                    uint32_t& o0, uint32_t& o1, uint32_t& o2,
@@ -239,79 +263,137 @@ __device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uin
   o3 = __builtin_amdgcn_perm(t23h, t01h, 0x07060302u);
 }
 
-template <bool kBf16, bool kTrans>
-__global__ __launch_bounds__(256) void quant_128x128_kernel(const void* __restrict__ w, int64_t ld_w,
-                                                            int64_t rows, int64_t cols,
-                                                            uint8_t* __restrict__ q, int64_t ld_q,
-                                                            float* __restrict__ scale,
-                                                            uint8_t* __restrict__ q_t, int64_t ld_qt,
-                                                            float* __restrict__ scale_t) {
-  __shared__ float red[4];
-  __shared__ uint32_t ct[kTrans ? 128 * kCPitch / 4 : 1];
+// Raw input of one 128x128 block held by one thread: its rows of 8 elements
+// as 16-byte (bf16) or 2 x 16-byte (f32) loads.
+template <bool kBf16, int kRows>
+struct RawRows {
+  u32x4 d[kRows][kBf16 ? 1 : 2];
+};
+
+template <bool kBf16, int kRows, int kRowStep>
+__device__ __forceinline__ void load_rows(RawRows<kBf16, kRows>& raw, const void* w, int64_t ld_w,
+                                          int64_t r0, int64_t c0, int rbase, int cc) {
   constexpr int kElt = kBf16 ? 2 : 4;
-  const int64_t c0 = int64_t(blockIdx.x) * 128;
-  const int64_t r0 = int64_t(blockIdx.y) * 128;
-  const int t = threadIdx.x;
-  const int cc = (t & 15) * 8;
-  const int rbase = t >> 4;
-
-  float v[8][8];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const char* src = static_cast<const char*>(w) + ((r0 + rbase + 16 * p) * ld_w + c0 + cc) * kElt;
-    load8<kBf16>(src, v[p]);
-  }
-  float m = 0.0f;
-#pragma unroll
-  for (int p = 0; p < 8; ++p) m = fmaxf(m, absmax8(v[p]));
-  m = wave_max(m);
-  if ((t & 63) == 0) red[t >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = tile_scale(m);
-  const float r = 1.0f / s;
-
-#pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const uint2 codes = encode8<kBf16>(v[p], s, r);
-    const int rr = rbase + 16 * p;
-    *reinterpret_cast<uint2*>(q + (r0 + rr) * ld_q + c0 + cc) = codes;
-    if constexpr (kTrans) {
-      ct[(rr * kCPitch + cc) / 4] = codes.x;
-      ct[(rr * kCPitch + cc) / 4 + 1] = codes.y;
-    }
-  }
-  if (t == 0) {
-    scale[blockIdx.y * (cols / 128) + blockIdx.x] = s;
-    if (scale_t) scale_t[blockIdx.x * (rows / 128) + blockIdx.y] = s;
-  }
-  if constexpr (kTrans) {
-    __syncthreads();
-    const int lane = t & 63;
-    const int a = (lane & 7) | ((lane >> 5) << 3);        // row octet 0..15
-    const int b = ((lane >> 3) & 3) | ((t >> 6) << 2);    // column octet 0..15
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = ((8 * a + i) * kCPitch + 8 * b) / 4;
-      lo[i] = ct[idx];
-      hi[i] = ct[idx + 1];
-    }
-    uint32_t col_lo[8], col_hi[8];   // column j: rows 0-3 in col_lo[j], rows 4-7 in col_hi[j]
-    transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3], col_lo[0], col_lo[1], col_lo[2], col_lo[3]);
-    transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7], col_hi[0], col_hi[1], col_hi[2], col_hi[3]);
-    transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3], col_lo[4], col_lo[5], col_lo[6], col_lo[7]);
-    transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], col_hi[4], col_hi[5], col_hi[6], col_hi[7]);
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      uint8_t* dst = q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a;
-      *reinterpret_cast<uint2*>(dst) = make_uint2(col_lo[jj], col_hi[jj]);
-    }
+  for (int p = 0; p < kRows; ++p) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(w) + ((r0 + rbase + kRowStep * p) * ld_w + c0 + cc) * kElt);
+    raw.d[p][0] = __builtin_nontemporal_load(src);
+    if constexpr (!kBf16) raw.d[p][1] = __builtin_nontemporal_load(src + 1);
   }
 }
 
-fp8bs_status check_matrix(const void* p, int64_t ld, int64_t cols, int elt, const char* name) {
+template <bool kBf16>
+__device__ __forceinline__ void unpack8(const u32x4 (&d)[kBf16 ? 1 : 2], float (&v)[8]) {
+  if constexpr (kBf16) {
+    v[0] = bf16_lo(d[0].x); v[1] = bf16_hi(d[0].x);
+    v[2] = bf16_lo(d[0].y); v[3] = bf16_hi(d[0].y);
+    v[4] = bf16_lo(d[0].z); v[5] = bf16_hi(d[0].z);
+    v[6] = bf16_lo(d[0].w); v[7] = bf16_hi(d[0].w);
+  } else {
+    v[0] = __uint_as_float(d[0].x); v[1] = __uint_as_float(d[0].y);
+    v[2] = __uint_as_float(d[0].z); v[3] = __uint_as_float(d[0].w);
+    v[4] = __uint_as_float(d[1].x); v[5] = __uint_as_float(d[1].y);
+    v[6] = __uint_as_float(d[1].z); v[7] = __uint_as_float(d[1].w);
+  }
+}
+
+// Workgroup g handles blocks g, g + gridDim.x, ... (block b = row block
+// b / col_blocks, column block b % col_blocks), reading block i + 1 into
+// registers while block i is reduced, encoded and stored, so that loads and
+// stores of different blocks overlap.
+template <bool kBf16, bool kTrans, int kThreads>
+__global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __restrict__ w, int64_t ld_w,
+                                                                 int64_t rows, int64_t cols,
+                                                                 uint8_t* __restrict__ q, int64_t ld_q,
+                                                                 float* __restrict__ scale,
+                                                                 uint8_t* __restrict__ q_t, int64_t ld_qt,
+                                                                 float* __restrict__ scale_t) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kRowStep = kThreads / 16;
+  constexpr int kRows = 128 / kRowStep;
+  __shared__ float red[kWaves];
+  __shared__ uint32_t ct[kTrans ? 128 * kCPitch / 4 : 1];
+  const int t = threadIdx.x;
+  const int cc = (t & 15) * 8;
+  const int rbase = t >> 4;
+  const uint32_t col_blocks = uint32_t(cols / 128);
+  const uint32_t n_blocks = uint32_t(rows / 128) * col_blocks;
+
+  RawRows<kBf16, kRows> cur, nxt;
+  uint32_t blk = blockIdx.x;
+  if (blk >= n_blocks) return;
+  load_rows<kBf16, kRows, kRowStep>(cur, w, ld_w, int64_t(blk / col_blocks) * 128,
+                                    int64_t(blk % col_blocks) * 128, rbase, cc);
+  for (; blk < n_blocks; blk += gridDim.x) {
+    const uint32_t bi = blk / col_blocks, bj = blk % col_blocks;
+    const int64_t r0 = int64_t(bi) * 128, c0 = int64_t(bj) * 128;
+    const uint32_t nb = blk + gridDim.x;
+    if (nb < n_blocks)
+      load_rows<kBf16, kRows, kRowStep>(nxt, w, ld_w, int64_t(nb / col_blocks) * 128,
+                                        int64_t(nb % col_blocks) * 128, rbase, cc);
+
+    float v[kRows][8];
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) unpack8<kBf16>(cur.d[p], v[p]);
+    float m = 0.0f;
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) m = fmaxf(m, absmax8(v[p]));
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) m = fmaxf(m, red[i]);
+    const float s = tile_scale(m);
+    const float r = 1.0f / s;
+
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) {
+      const uint2 codes = encode8<kBf16>(v[p], s, r);
+      const int rr = rbase + kRowStep * p;
+      store_codes8(q + (r0 + rr) * ld_q + c0 + cc, codes);
+      if constexpr (kTrans) {
+        ct[(rr * kCPitch + cc) / 4] = codes.x;
+        ct[(rr * kCPitch + cc) / 4 + 1] = codes.y;
+      }
+    }
+    if (t == 0) {
+      scale[bi * col_blocks + bj] = s;
+      if (scale_t) scale_t[bj * (rows / 128) + bi] = s;
+    }
+    __syncthreads();   // red (and ct) are reused by the next block
+    if constexpr (kTrans) {
+      if (t < 256) {
+        const int lane = t & 63;
+        const int a = (lane & 7) | ((lane >> 5) << 3);        // row octet 0..15
+        const int b = ((lane >> 3) & 3) | ((t >> 6) << 2);    // column octet 0..15
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int idx = ((8 * a + i) * kCPitch + 8 * b) / 4;
+          lo[i] = ct[idx];
+          hi[i] = ct[idx + 1];
+        }
+        uint32_t col_lo[8], col_hi[8];   // column j: rows 0-3 in col_lo[j], rows 4-7 in col_hi[j]
+        transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3], col_lo[0], col_lo[1], col_lo[2], col_lo[3]);
+        transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7], col_hi[0], col_hi[1], col_hi[2], col_hi[3]);
+        transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3], col_lo[4], col_lo[5], col_lo[6], col_lo[7]);
+        transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], col_hi[4], col_hi[5], col_hi[6], col_hi[7]);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          store_codes8(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
+      }
+      __syncthreads();   // ct is rewritten by the next block
+    }
+    cur = nxt;
+  }
+}
+
+fp8bs_status check_matrix(const void* p, int64_t rows, int64_t ld, int64_t cols, int elt, const char* name) {
   if (ld < cols) return fail(FP8BS_ERR_INVALID_ARG, "%s: pitch %lld < columns %lld", name, (long long)ld, (long long)cols);
+  if (!sane_matrix(rows, ld, elt))
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: %lld rows of pitch %lld exceed any allocation", name, (long long)rows, (long long)ld);
   if (!aligned16(p) || (ld * elt) % 16 != 0)
     return fail(FP8BS_ERR_ALIGNMENT, "%s: pointer and row pitch must be 16-byte aligned", name);
   return FP8BS_OK;
@@ -336,9 +418,9 @@ extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int6
   if (rows == 0 || cols == 0) return FP8BS_OK;
   if (!x || !q || !scale) return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
   const int elt = elem_size(x_dtype);
-  fp8bs_status st = check_matrix(x, ld_x, cols, elt, "x");
+  fp8bs_status st = check_matrix(x, rows, ld_x, cols, elt, "x");
   if (st != FP8BS_OK) return st;
-  st = check_matrix(q, ld_q, t128x1 ? rows : cols, 1, "q");
+  st = check_matrix(q, t128x1 ? cols : rows, ld_q, t128x1 ? rows : cols, 1, "q");
   if (st != FP8BS_OK) return st;
   if (!aligned4(scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
 
@@ -379,26 +461,31 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
     return fail(FP8BS_ERR_SHAPE, "%s: rows %lld and cols %lld must be multiples of 128", fn, (long long)rows, (long long)cols);
   if (rows == 0 || cols == 0) return FP8BS_OK;
   if (!w || !q || !scale) return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
-  fp8bs_status st = check_matrix(w, ld_w, cols, elem_size(w_dtype), "w");
+  fp8bs_status st = check_matrix(w, rows, ld_w, cols, elem_size(w_dtype), "w");
   if (st != FP8BS_OK) return st;
-  st = check_matrix(q, ld_q, cols, 1, "q");
+  st = check_matrix(q, rows, ld_q, cols, 1, "q");
   if (st != FP8BS_OK) return st;
   if (q_t) {
-    st = check_matrix(q_t, ld_qt, rows, 1, "q_t");
+    st = check_matrix(q_t, cols, ld_qt, rows, 1, "q_t");
     if (st != FP8BS_OK) return st;
   }
   if (!aligned4(scale) || (scale_t && !aligned4(scale_t)))
     return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
-  if (rows / 128 > 65535) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many block rows", fn);
-  const dim3 grid(static_cast<uint32_t>(cols / 128), static_cast<uint32_t>(rows / 128));
+  // One block per workgroup up to FP8BS_W_GRID blocks; beyond that each
+  // workgroup takes ceil(blocks / FP8BS_W_GRID) blocks in turn.
+  const int64_t n_blocks = (rows / 128) * (cols / 128);
+  if (n_blocks > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many blocks", fn);
+  const int64_t per_wg = (n_blocks + FP8BS_W_GRID - 1) / FP8BS_W_GRID;
+  const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
   const bool bf16 = w_dtype == FP8BS_BF16;
+  constexpr int kT = FP8BS_W_THREADS;
   if (bf16 && q_t)
-    hipLaunchKernelGGL((quant_128x128_kernel<true, true>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+    hipLaunchKernelGGL((quant_128x128_kernel<true, true, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   else if (bf16)
-    hipLaunchKernelGGL((quant_128x128_kernel<true, false>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+    hipLaunchKernelGGL((quant_128x128_kernel<true, false, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   else if (q_t)
-    hipLaunchKernelGGL((quant_128x128_kernel<false, true>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+    hipLaunchKernelGGL((quant_128x128_kernel<false, true, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   else
-    hipLaunchKernelGGL((quant_128x128_kernel<false, false>), grid, dim3(256), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+    hipLaunchKernelGGL((quant_128x128_kernel<false, false, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   return check_launch(fn);
 }

@@ -16,6 +16,16 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 inline int elem_size(int32_t dtype) { return dtype == FP8BS_BF16 ? 2 : 4; }
+
+// A row count or pitch beyond these cannot describe a real allocation (a
+// 64-bit argument passed as a 32-bit value can leave garbage in its upper
+// half); such calls are rejected instead of launching with wild addresses.
+constexpr int64_t kMaxExtent = int64_t(1) << 31;   // elements per dimension
+constexpr int64_t kMaxBytes = int64_t(1) << 47;    // bytes spanned by one matrix
+inline bool sane_matrix(int64_t rows, int64_t ld, int elt) {
+  return rows >= 0 && ld >= 0 && rows <= kMaxExtent && ld <= kMaxExtent &&
+         rows * ld <= kMaxBytes / elt;
+}
 inline bool valid_dtype(int32_t dtype) { return dtype == FP8BS_BF16 || dtype == FP8BS_F32; }
 
 }  // namespace fp8bs

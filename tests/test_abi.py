@@ -104,6 +104,18 @@ def test_grouped_validation(L):
     assert _grouped(L, ydt=4) == INVALID and _grouped(L, accum=3) == INVALID
 
 
+def test_absurd_pitches_rejected(L):
+    """A 64-bit size whose upper half is garbage (as when a caller passes a
+    32-bit value) must be refused before any launch."""
+    big = (1 << 40) + 256
+    assert _act(L, ldx=big) == INVALID and _act(L, ldq=big) == INVALID
+    assert _act(L, tiling=1, rows=128, cols=8, ldx=8, ldq=big) == INVALID
+    assert _w(L, ldw=big) == INVALID and _w(L, qt=A16, ldqt=big) == INVALID
+    assert _gemm(L, ldy=big) == INVALID and _gemm(L, lda=big) == INVALID
+    assert _gemm(L, M=(1 << 33)) == INVALID
+    assert _grouped(L, M=(1 << 40)) == INVALID
+
+
 def test_last_error_is_per_call_text(L):
     assert _gemm(L, K=100, lda=112, ldb=112) == SHAPE
     assert "K=100" in fb.last_error()
