@@ -32,10 +32,14 @@ PEAK_F16_TFLOPS = 2500.0        # MI355X dense f16/bf16 MFMA (the FP32-accumulat
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
 
-# HBM bytes per GEMM launch from rocprofv3 --pmc FETCH_SIZE + WRITE_SIZE, scaled
-# by the counters' reading for a copy kernel of known size; valid only for the
-# GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": None, "bytes_per_launch": None}
+# HBM bytes per GEMM launch from two rocprofv3 --pmc runs of
+# `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
+# the same counter reads for the device copy of known size that --calib-copy
+# adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
+TRAFFIC = {"gemm_sha256": "fa7a1e9b0534c44c96dab4052eb5c5614beececd75c924cfbe410eb387737eef",
+           "bytes_per_launch": 137155877,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.80 MB written
+           "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
+CALIB_COPY_BYTES = 128 << 20
 
 
 def algorithmic():
@@ -57,8 +61,10 @@ def parse():
     p.add_argument("--rotate-mib", type=int, default=1100,
                    help="bytes of input/output buffers cycled through (defeats the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=1024,
-                   help="rows of X in the oracle's timed sample")
+    p.add_argument("--cpu-rows", type=int, default=M,
+                   help="rows of X in the oracle's timed sample (default: all)")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run one device copy of 128 MiB (counter calibration for rocprofv3 --pmc)")
     return p.parse_args()
 
 
@@ -145,6 +151,12 @@ def main():
 
     step(0)
     torch.cuda.synchronize()
+    if args.calib_copy:
+        src = torch.empty(CALIB_COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     print(f"[bench] warmup {args.warmup} steps, {n_sets} buffer sets "
           f"({n_sets * set_bytes / 2**20:.0f} MiB cycled)", file=sys.stderr, flush=True)
