@@ -31,11 +31,12 @@ from .quantize import (SCALE_GUARD, tile_scale, quant_1x128, quant_128x1_t,
                        quant_128x128, dequant_1x128, dequant_128x128)
 from .gemm import (blockscaled_gemm_ref, grouped_gemm_ref,
                    blockscaled_gemm_fp32_model, gemm_tolerance_ok)
+from .dequant import dequant_f32, dequant_bf16, f32_to_bf16_rne
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_magnitudes", "e4m3_half_ulp",
     "SCALE_GUARD", "tile_scale", "quant_1x128", "quant_128x1_t", "quant_128x128",
     "dequant_1x128", "dequant_128x128",
     "blockscaled_gemm_ref", "grouped_gemm_ref", "blockscaled_gemm_fp32_model",
-    "gemm_tolerance_ok",
+    "gemm_tolerance_ok", "dequant_f32", "dequant_bf16", "f32_to_bf16_rne",
 ]
