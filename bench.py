@@ -212,6 +212,48 @@ def main():
     g1.record(stream)
     torch.cuda.synchronize()
     alt_us = g0.elapsed_time(g1) / n_alt * 1e3
+    # Further kernels of the path, timed on the rotating X buffers with events
+    # on the launch stream: the dual-orientation quantizer (1x128 and 128x1
+    # transposed from one read) and, for comparison, the 128x1 tiling alone.
+    def timed_us(fn, n=50, warm=5):
+        for i in range(warm):
+            fn(i)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(n):
+            fn(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n * 1e3
+
+    qd = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sd = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    qtd = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    std = torch.empty((K, M // 128), dtype=torch.float32, device=dev)
+
+    def dual(i):
+        if L.fp8_quant_act_dual(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, vp(qd.data_ptr()), K,
+                                vp(sd.data_ptr()), vp(qtd.data_ptr()), M, vp(std.data_ptr()), hs):
+            raise RuntimeError(fb.last_error())
+
+    def t128x1(i):
+        if L.fp8_quant_act_1x128(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 1, vp(qtd.data_ptr()), M,
+                                 vp(std.data_ptr()), hs):
+            raise RuntimeError(fb.last_error())
+
+    n_deq = 4                       # 4 x (29 MB codes + 59 MB bf16 out) cycled: above the MALL
+    deq_in = [a.clone() for _ in range(n_deq)]
+    deq_out = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(n_deq)]
+
+    def dequant(i):
+        if L.fp8_dequant(vp(deq_in[i % n_deq].data_ptr()), M, K, K, vp(sa.data_ptr()), 0,
+                         vp(deq_out[i % n_deq].data_ptr()), 0, K, hs):
+            raise RuntimeError(fb.last_error())
+
+    dual_us, t128_us, deq_us = timed_us(dual), timed_us(t128x1), timed_us(dequant)
+    deq_bytes = M * K * (1 + 2) + 4 * M * (K // 128)
+    dual_bytes = M * K * (2 + 1 + 1) + 2 * 4 * M * (K // 128)
+    t128_bytes = qx_bytes
     qx_gbps = qx_bytes / (avg_ms[0] * 1e-3) / 1e9
     qw_gbps = qw_bytes / (avg_ms[1] * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12
@@ -252,6 +294,19 @@ def main():
                                  "TFLOP/s": round(gemm_tflops, 2),
                                  "frac_own_peak": round(gemm_tflops / peak, 4),
                                  "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "flops": flops},
+            "quant_act_dual": {"avg_us": round(dual_us, 2),
+                               "GB/s": round(dual_bytes / dual_us / 1e3, 1),
+                               "frac_hbm": round(dual_bytes / dual_us / 1e3 / PEAK_HBM_GBPS, 4),
+                               "bytes": dual_bytes, "launches": 50,
+                               "note": "X 1x128 and 128x1 (transposed) from one read"},
+            "quant_act_128x1_t": {"avg_us": round(t128_us, 2),
+                                  "GB/s": round(t128_bytes / t128_us / 1e3, 1),
+                                  "frac_hbm": round(t128_bytes / t128_us / 1e3 / PEAK_HBM_GBPS, 4),
+                                  "bytes": t128_bytes, "launches": 50},
+            "dequant_1x128_bf16": {"avg_us": round(deq_us, 2),
+                                   "GB/s": round(deq_bytes / deq_us / 1e3, 1),
+                                   "frac_hbm": round(deq_bytes / deq_us / 1e3 / PEAK_HBM_GBPS, 4),
+                                   "bytes": deq_bytes, "launches": 50},
             "blockscaled_gemm_other_accum": {
                 "accum": "fp8_mfma" if args.accum == "fp32" else "fp32", "avg_us": round(alt_us, 2),
                 "TFLOP/s": round(flops / (alt_us * 1e-6) / 1e12, 2), "launches": n_alt},

@@ -19,7 +19,8 @@ import os
 import re
 
 __all__ = [
-    "fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_blockscaled_gemm",
+    "fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
+    "fp8_blockscaled_gemm",
     "fp8_blockscaled_grouped_gemm", "last_error", "version", "lib", "lib_path",
     "Fp8bsError", "STATUS",
 ]
@@ -29,7 +30,7 @@ _LIB_NAME = "libfp8bs.so"
 
 STATUS = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "ALIGNMENT", 4: "UNSUPPORTED", 5: "HIP"}
 BF16, F32 = 0, 1
-TILE_1x128, TILE_128x1_T = 0, 1
+TILE_1x128, TILE_128x1_T, TILE_128x128 = 0, 1, 2
 BSCALE_BLOCK128, BSCALE_ROW = 0, 1
 ACCUM_FP32, ACCUM_FP8_MFMA = 0, 1
 _ACCUM = {"fp32": ACCUM_FP32, "fp8_mfma": ACCUM_FP8_MFMA}
@@ -60,10 +61,12 @@ def lib():
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     L.fp8_quant_act_1x128.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
     L.fp8_quant_w_128x128.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
+    L.fp8_quant_act_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
+    L.fp8_dequant.argtypes = [vp, i64, i64, i64, vp, i32, vp, i32, i64, vp]
     L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, i32, vp]
     L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp]
-    for f in ("fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_blockscaled_gemm",
-              "fp8_blockscaled_grouped_gemm"):
+    for f in ("fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
+              "fp8_blockscaled_gemm", "fp8_blockscaled_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int
     L.fp8bs_last_error.restype = ctypes.c_char_p
     L.fp8bs_last_error.argtypes = []
@@ -165,6 +168,35 @@ def fp8_quant_act_1x128(x, tiling="1x128", q=None, scale=None):
     return q, scale
 
 
+def fp8_quant_act_dual(x, q=None, scale=None, q_t=None, scale_t=None):
+    """Both activation tilings from one read of x: returns (q [rows, cols],
+    scale [rows, cols/128]) of the 1x128 tiling and (q_t [cols, rows],
+    scale_t [cols, rows/128]) of the 128x1 tiling written transposed."""
+    torch = _torch()
+    _on_gpu(x, q, scale, q_t, scale_t)
+    rows, cols = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((rows, cols // 128), dtype=torch.float32, device=dev)
+    if q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
+    if scale_t is None:
+        scale_t = torch.empty((cols, rows // 128), dtype=torch.float32, device=dev)
+    _need(q, (rows, cols), torch.uint8, "q")
+    _need(scale, (rows, cols // 128), torch.float32, "scale")
+    _need(q_t, (cols, rows), torch.uint8, "q_t")
+    _need(scale_t, (cols, rows // 128), torch.float32, "scale_t")
+    for t, nm in ((scale, "scale"), (scale_t, "scale_t")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    _check(lib().fp8_quant_act_dual(_ptr(x), _dtype_code(x, "x"), rows, cols, _pitch(x, "x"),
+                                    _ptr(q), _pitch(q, "q"), _ptr(scale), _ptr(q_t),
+                                    _pitch(q_t, "q_t"), _ptr(scale_t), _stream()))
+    return q, scale, q_t, scale_t
+
+
 def fp8_quant_w_128x128(w, transpose=False, q=None, scale=None, q_t=None, scale_t=None):
     """128x128 block quantization; with transpose=True also the transposed codes
     [cols, rows] and scales [cols/128, rows/128].  Returns (q, scale, q_t, scale_t)."""
@@ -195,6 +227,29 @@ def fp8_quant_w_128x128(w, transpose=False, q=None, scale=None, q_t=None, scale_
                                      _ptr(q), _pitch(q, "q"), _ptr(scale), _ptr(q_t), ld_qt,
                                      _ptr(scale_t), _stream()))
     return q, scale, q_t, scale_t
+
+
+def fp8_dequant(q, scale, tiling="1x128", out_dtype=None, y=None):
+    """y = fl32(e4m3(q) * scale of its tile) (bf16: that float32 rounded to
+    nearest even).  tiling "1x128": scale [rows, cols/128]; "128x128":
+    scale [rows/128, cols/128]."""
+    torch = _torch()
+    _on_gpu(q, scale, y)
+    rows, cols = q.shape
+    if out_dtype is None:
+        out_dtype = torch.float32 if y is None else y.dtype
+    if y is None:
+        y = torch.empty((rows, cols), dtype=out_dtype, device=q.device)
+    tcode = {"1x128": TILE_1x128, "128x128": TILE_128x128}[tiling]
+    sshape = (rows, cols // 128) if tcode == TILE_1x128 else (rows // 128, cols // 128)
+    _need(q, (rows, cols), torch.uint8, "q")
+    _need(scale, sshape, torch.float32, "scale")
+    _need(y, (rows, cols), y.dtype, "y")
+    if not scale.is_contiguous():
+        raise ValueError("scale must be contiguous")
+    _check(lib().fp8_dequant(_ptr(q), rows, cols, _pitch(q, "q"), _ptr(scale), tcode, _ptr(y),
+                             _dtype_code(y, "y"), _pitch(y, "y"), _stream()))
+    return y
 
 
 def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None,

@@ -248,6 +248,12 @@ constexpr int kCPitch = 132;  // bytes
 #ifndef FP8BS_W_GRID
 #define FP8BS_W_GRID 65536
 #endif
+#ifndef FP8BS_DUAL_THREADS
+#define FP8BS_DUAL_THREADS 256
+#endif
+#ifndef FP8BS_DUAL_GRID
+#define FP8BS_DUAL_GRID 65536
+#endif
 
 __device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
                                                    uint32_t& o0, uint32_t& o1, uint32_t& o2,
@@ -390,6 +396,149 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Both activation tilings of one tensor from a single read of it: 1x128 tiles
+// along the rows (codes q [rows, cols], scales [rows, cols/128]) and 128x1
+// tiles along the columns, written transposed (codes q_t = codes of x^T
+// [cols, rows], scales [cols, rows/128]).  A workgroup of kThreads threads
+// takes one 128x128 block of x at a time (block b: row block b / col_blocks,
+// column block b % col_blocks) and holds it as the 128x128 kernel does:
+// thread t owns columns 8 (t % 16) .. + 7 of rows t / 16 + (kThreads / 16) p.
+//  - 1x128 tiles: the 16 lanes of a DPP row hold one row of the block, which
+//    is one tile; row16_max gives its amax and the codes are stored straight
+//    from registers.
+//  - 128x1 tiles: each thread takes the maxima of its 8 columns over its
+//    rows, then over the four 16-lane groups of its wave (xor 16, 32) and
+//    over the waves through LDS.  The first 128 threads turn the column
+//    maxima into scales; every thread encodes its values with its columns'
+//    scales into an LDS byte tile, and 8x8 byte transposes turn that into
+//    whole 128-byte rows of q_t.
+// The next block's input is loaded into registers while the current one is
+// processed.  Three barriers per block; the LDS buffers written after each
+// one were last read before the previous one.
+template <bool kBf16, int kThreads>
+__global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __restrict__ x, int64_t ld_x,
+                                                              int64_t rows, int64_t cols,
+                                                              uint8_t* __restrict__ q, int64_t ld_q,
+                                                              float* __restrict__ scale,
+                                                              uint8_t* __restrict__ q_t, int64_t ld_qt,
+                                                              float* __restrict__ scale_t) {
+  constexpr int kWaves = kThreads / 64;
+  constexpr int kRowStep = kThreads / 16;
+  constexpr int kRows = 128 / kRowStep;
+  static_assert(kThreads >= 256 && kThreads % 256 == 0 && kRows >= 1, "block layout");
+  __shared__ __align__(16) float cmax[kWaves][128];
+  __shared__ float csc[2][128];                 // column scales and their reciprocals
+  __shared__ uint32_t ct[128 * kCPitch / 4];    // 128x1 codes, [row][column] bytes
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int cc = (t & 15) * 8;
+  const int rbase = t >> 4;
+  const uint32_t col_blocks = uint32_t(cols / 128);
+  const uint32_t n_blocks = uint32_t(rows / 128) * col_blocks;
+  const int64_t row_kb = cols / 128;   // scale columns of the 1x128 tiling
+  const int64_t col_kb = rows / 128;   // scale columns of the 128x1 tiling
+
+  RawRows<kBf16, kRows> cur, nxt;
+  uint32_t blk = blockIdx.x;
+  if (blk >= n_blocks) return;
+  load_rows<kBf16, kRows, kRowStep>(cur, x, ld_x, int64_t(blk / col_blocks) * 128,
+                                    int64_t(blk % col_blocks) * 128, rbase, cc);
+  for (; blk < n_blocks; blk += gridDim.x) {
+    const uint32_t bi = blk / col_blocks, bj = blk % col_blocks;
+    const int64_t r0 = int64_t(bi) * 128, c0 = int64_t(bj) * 128;
+    const uint32_t nb = blk + gridDim.x;
+    if (nb < n_blocks)
+      load_rows<kBf16, kRows, kRowStep>(nxt, x, ld_x, int64_t(nb / col_blocks) * 128,
+                                        int64_t(nb % col_blocks) * 128, rbase, cc);
+    float v[kRows][8];
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) unpack8<kBf16>(cur.d[p], v[p]);
+
+    // 1x128 tiles.
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) {
+      const float s = tile_scale(row16_max(absmax8(v[p])));
+      const float r = 1.0f / s;
+      const int64_t row = r0 + rbase + kRowStep * p;
+      store_codes8(q + row * ld_q + c0 + cc, encode8<kBf16>(v[p], s, r));
+      if ((t & 15) == 0) store_scale(&scale[row * row_kb + bj], s);
+    }
+
+    // 128x1 tiles: column maxima.
+    float cm[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float m = fabsf(v[0][i]);
+#pragma unroll
+      for (int p = 1; p < kRows; ++p) m = fmaxf(m, fabsf(v[p][i]));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      cm[i] = fmaxf(m, __shfl_xor(m, 32));
+    }
+    if (lane < 16) {
+      float4* dst = reinterpret_cast<float4*>(&cmax[wave][cc]);
+      dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+      dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+    }
+    __syncthreads();
+    if (t < 128) {
+      float m = cmax[0][t];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) m = fmaxf(m, cmax[w][t]);
+      const float s = tile_scale(m);
+      csc[0][t] = s;
+      csc[1][t] = 1.0f / s;
+      store_scale(&scale_t[(c0 + t) * col_kb + bi], s);
+    }
+    __syncthreads();
+
+    // 128x1 codes into the LDS byte tile.
+    float cs[8], cr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      cs[i] = csc[0][cc + i];
+      cr[i] = csc[1][cc + i];
+    }
+#pragma unroll
+    for (int p = 0; p < kRows; ++p) {
+      float qv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[i] = quotient<kBf16>(v[p][i], cs[i], cr[i]);
+      const int rr = rbase + kRowStep * p;
+      ct[(rr * kCPitch + cc) / 4] = pack4_e4m3(qv[0], qv[1], qv[2], qv[3]);
+      ct[(rr * kCPitch + cc) / 4 + 1] = pack4_e4m3(qv[4], qv[5], qv[6], qv[7]);
+    }
+    __syncthreads();
+
+    // Transposed store: thread u < 256 takes the 8x8 byte sub-block (row
+    // octet a, column octet b); lanes 0-7 and 32-39 of a wave cover the 16
+    // row octets of one column octet, so every store instruction writes
+    // whole 128-byte rows of q_t.
+    if (t < 256) {
+      const int a = (lane & 7) | ((lane >> 5) << 3);
+      const int b = ((lane >> 3) & 3) | ((t >> 6) << 2);
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int idx = ((8 * a + i) * kCPitch + 8 * b) / 4;
+        lo[i] = ct[idx];
+        hi[i] = ct[idx + 1];
+      }
+      uint32_t col_lo[8], col_hi[8];
+      transpose4x4_bytes(lo[0], lo[1], lo[2], lo[3], col_lo[0], col_lo[1], col_lo[2], col_lo[3]);
+      transpose4x4_bytes(lo[4], lo[5], lo[6], lo[7], col_hi[0], col_hi[1], col_hi[2], col_hi[3]);
+      transpose4x4_bytes(hi[0], hi[1], hi[2], hi[3], col_lo[4], col_lo[5], col_lo[6], col_lo[7]);
+      transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], col_hi[4], col_hi[5], col_hi[6], col_hi[7]);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        store_codes8(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
+    }
+    cur = nxt;
+  }
+}
+
 fp8bs_status check_matrix(const void* p, int64_t rows, int64_t ld, int64_t cols, int elt, const char* name) {
   if (ld < cols) return fail(FP8BS_ERR_INVALID_ARG, "%s: pitch %lld < columns %lld", name, (long long)ld, (long long)cols);
   if (!sane_matrix(rows, ld, elt))
@@ -487,5 +636,36 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
     hipLaunchKernelGGL((quant_128x128_kernel<false, true, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   else
     hipLaunchKernelGGL((quant_128x128_kernel<false, false, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  return check_launch(fn);
+}
+
+extern "C" fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                           int64_t ld_x, uint8_t* q, int64_t ld_q, float* scale,
+                                           uint8_t* q_t, int64_t ld_qt, float* scale_t,
+                                           hipStream_t stream) {
+  const char* fn = "fp8_quant_act_dual";
+  if (!valid_dtype(x_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown x_dtype %d", fn, x_dtype);
+  if (rows < 0 || cols < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (rows % 128 || cols % 128)
+    return fail(FP8BS_ERR_SHAPE, "%s: rows %lld and cols %lld must be multiples of 128", fn, (long long)rows, (long long)cols);
+  if (rows == 0 || cols == 0) return FP8BS_OK;
+  if (!x || !q || !scale || !q_t || !scale_t) return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fp8bs_status st = check_matrix(x, rows, ld_x, cols, elem_size(x_dtype), "x");
+  if (st != FP8BS_OK) return st;
+  st = check_matrix(q, rows, ld_q, cols, 1, "q");
+  if (st != FP8BS_OK) return st;
+  st = check_matrix(q_t, cols, ld_qt, rows, 1, "q_t");
+  if (st != FP8BS_OK) return st;
+  if (!aligned4(scale) || !aligned4(scale_t))
+    return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
+  const int64_t n_blocks = (rows / 128) * (cols / 128);
+  if (n_blocks > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many blocks", fn);
+  const int64_t per_wg = (n_blocks + FP8BS_DUAL_GRID - 1) / FP8BS_DUAL_GRID;
+  const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
+  constexpr int kT = FP8BS_DUAL_THREADS;
+  if (x_dtype == FP8BS_BF16)
+    hipLaunchKernelGGL((quant_dual_kernel<true, kT>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  else
+    hipLaunchKernelGGL((quant_dual_kernel<false, kT>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   return check_launch(fn);
 }

@@ -61,7 +61,8 @@ typedef enum fp8bs_dtype { FP8BS_BF16 = 0, FP8BS_F32 = 1 } fp8bs_dtype;
 
 typedef enum fp8bs_act_tiling {
   FP8BS_TILE_1x128 = 0,        /* 128 consecutive elements of a row */
-  FP8BS_TILE_128x1_T = 1       /* 128 consecutive rows of a column; codes written transposed */
+  FP8BS_TILE_128x1_T = 1,      /* 128 consecutive rows of a column; codes written transposed */
+  FP8BS_TILE_128x128 = 2       /* 128x128 blocks (weights); accepted by fp8_dequant */
 } fp8bs_act_tiling;
 
 typedef enum fp8bs_bscale_kind {
@@ -123,6 +124,47 @@ fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, i
                                  int64_t ld_w, uint8_t* q, int64_t ld_q, float* scale,
                                  uint8_t* q_t, int64_t ld_qt, float* scale_t,
                                  hipStream_t stream);
+
+/*
+ * Both activation tilings of one tensor in a single pass over it: what
+ * fp8_quant_act_1x128 writes with FP8BS_TILE_1x128 and with
+ * FP8BS_TILE_128x1_T, from one read of x.  The backward pass needs both for
+ * the same tensor (codingmall "Unified E4M3 Format": the data-gradient GEMM
+ * contracts the output gradient over its columns, the weight-gradient GEMM
+ * over its rows/tokens; "Finkornig kvantisering" fixes the 1x128 tiles).
+ *
+ * x:       [rows, cols] of x_dtype, pitch ld_x >= cols; rows % 128 == 0 and
+ *          cols % 128 == 0.
+ * q:       [rows, cols] uint8, pitch ld_q >= cols (1x128 tiles along rows);
+ * scale:   [rows, cols/128] float32.
+ * q_t:     [cols, rows] uint8, pitch ld_qt >= rows: codes of x^T (128x1
+ *          tiles of x, i.e. 1x128 tiles of x^T);
+ * scale_t: [cols, rows/128] float32.
+ * Every output is required (non-NULL) and must not overlap another.  Codes
+ * and scales are bit-identical to the two single-tiling calls.
+ */
+fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                                int64_t ld_x, uint8_t* q, int64_t ld_q, float* scale,
+                                uint8_t* q_t, int64_t ld_qt, float* scale_t,
+                                hipStream_t stream);
+
+/*
+ * Dequantization (HolySheep (zh) section 2.2, FP8BlockQuantizer.dequantize:
+ * each code's value times its tile's stored scale):
+ *   y[r,c] = fl32(e4m3(q[r,c]) * s),  bf16 output: that float32 rounded to
+ *   nearest even.  The product is exact before its one float32 rounding.
+ *
+ * q:       [rows, cols] uint8 codes, pitch ld_q >= cols; cols % 128 == 0.
+ * scale:   tiling FP8BS_TILE_1x128:   [rows, cols/128] float32;
+ *          tiling FP8BS_TILE_128x128: [rows/128, cols/128] (rows % 128 == 0).
+ *          (The output of the 128x1_T tiling is the 1x128 tiling of x^T:
+ *          pass it as FP8BS_TILE_1x128 to get x^T back.)
+ * y:       [rows, cols] of y_dtype, pitch ldy >= cols.
+ * NaN codes (S.1111.111) give NaN.
+ */
+fp8bs_status fp8_dequant(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q,
+                         const float* scale, int32_t tiling, void* y, int32_t y_dtype,
+                         int64_t ldy, hipStream_t stream);
 
 /*
  * Block-scaled FP8 GEMM with FP32 promotion per 128-deep K block

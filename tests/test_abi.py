@@ -20,8 +20,9 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = fb.header_functions()
-    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_w_128x128", "fp8_blockscaled_gemm",
-                          "fp8_blockscaled_grouped_gemm", "fp8bs_last_error", "fp8bs_version"}
+    assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128",
+                          "fp8_dequant", "fp8_blockscaled_gemm", "fp8_blockscaled_grouped_gemm",
+                          "fp8bs_last_error", "fp8bs_version"}
     for n in names:
         assert hasattr(L, n), n
     assert "gfx950" in fb.version()
@@ -66,6 +67,45 @@ def test_quant_w_validation(L):
     assert _w(L, qt=A16, ldqt=264) == ALIGN
     assert _w(L, s=A16 + 1) == ALIGN
     assert _w(L, qt=A16, ldqt=256, st=A4 + 1) == ALIGN
+
+
+def _dual(L, x=A16, dt=0, rows=256, cols=384, ldx=384, q=A16, ldq=384, s=A16, qt=A16, ldqt=256,
+          st=A16):
+    return L.fp8_quant_act_dual(x, dt, rows, cols, ldx, q, ldq, s, qt, ldqt, st, None)
+
+
+def test_quant_dual_validation(L):
+    assert _dual(L, rows=0) == OK and _dual(L, cols=0) == OK
+    assert _dual(L, rows=0, x=NULL, q=NULL, s=NULL, qt=NULL, st=NULL) == OK
+    assert _dual(L, dt=2) == INVALID and _dual(L, rows=-128) == INVALID
+    assert _dual(L, rows=200) == SHAPE and _dual(L, cols=100, ldx=112) == SHAPE
+    for kw in ("x", "q", "s", "qt", "st"):                              # every output required
+        assert _dual(L, **{kw: NULL}) == INVALID, kw
+    assert _dual(L, ldx=256) == INVALID and _dual(L, ldq=256) == INVALID
+    assert _dual(L, ldqt=128) == INVALID                                # ld_qt < rows
+    assert _dual(L, x=A16 + 8) == ALIGN and _dual(L, q=A16 + 4) == ALIGN
+    assert _dual(L, qt=A16 + 2) == ALIGN and _dual(L, ldqt=264) == ALIGN
+    assert _dual(L, s=A16 + 1) == ALIGN and _dual(L, st=A4 + 2) == ALIGN
+    assert _dual(L, ldx=(1 << 40) + 384) == INVALID
+
+
+def _deq(L, q=A16, rows=256, cols=384, ldq=384, s=A16, tiling=0, y=A16, ydt=1, ldy=384):
+    return L.fp8_dequant(q, rows, cols, ldq, s, tiling, y, ydt, ldy, None)
+
+
+def test_dequant_validation(L):
+    assert _deq(L, rows=0) == OK and _deq(L, rows=0, q=NULL, s=NULL, y=NULL) == OK
+    assert _deq(L, tiling=1) == INVALID and _deq(L, tiling=3) == INVALID
+    assert "x^T" in fb.last_error() or "tiling" in fb.last_error()
+    assert _deq(L, ydt=5) == INVALID and _deq(L, rows=-1) == INVALID
+    assert _deq(L, cols=200, ldq=208, ldy=208) == SHAPE
+    assert _deq(L, tiling=2, rows=200) == SHAPE
+    assert _deq(L, q=NULL) == INVALID and _deq(L, s=NULL) == INVALID and _deq(L, y=NULL) == INVALID
+    assert _deq(L, ldq=256) == INVALID and _deq(L, ldy=256) == INVALID
+    assert _deq(L, q=A16 + 8) == ALIGN and _deq(L, y=A16 + 4) == ALIGN
+    assert _deq(L, ldq=392) == ALIGN and _deq(L, ydt=0, ldy=388) == ALIGN   # 776 B bf16 rows
+    assert _deq(L, s=A16 + 2) == ALIGN
+    assert _deq(L, ldq=(1 << 40) + 384) == INVALID
 
 
 def _gemm(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, y=A16,
