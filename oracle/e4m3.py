@@ -65,6 +65,8 @@ def e4m3_encode(v):
     even code.
     """
     v = np.asarray(v, dtype=np.float32)
+    shape = v.shape
+    v = v.reshape(-1)                  # elementwise; one flat pass is much faster in numpy
     a = np.abs(v).astype(np.float64)
     sign = np.signbit(v).astype(np.uint8) << 7
     mags = e4m3_magnitudes()
@@ -79,7 +81,7 @@ def e4m3_encode(v):
     code = np.where(a_clip == mags[hi], hi, code)   # exact hits (incl. 0)
     code = np.where(a > E4M3_MAX, 126, code)          # saturate, incl. inf
     code = np.where(np.isnan(a), 127, code)           # NaN keeps its sign
-    return (code.astype(np.uint8) | sign).astype(np.uint8)
+    return (code.astype(np.uint8) | sign).astype(np.uint8).reshape(shape)
 
 
 def e4m3_half_ulp(v):
