@@ -36,8 +36,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "fa7a1e9b0534c44c96dab4052eb5c5614beececd75c924cfbe410eb387737eef",
-           "bytes_per_launch": 137155877,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.80 MB written
+TRAFFIC = {"gemm_sha256": "170c1c827b8f20c400b16b0089f971da3de61fbecae92175634aa7d7700492b3",
+           "bytes_per_launch": 137163276,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.81 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
@@ -250,6 +250,28 @@ def main():
                          vp(deq_out[i % n_deq].data_ptr()), 0, K, hs):
             raise RuntimeError(fb.last_error())
 
+    # The GEMM with its output quantized 1x128 in the epilogue, against the
+    # same result in two launches (float32 GEMM output, then the quantizer).
+    yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    ysc = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
+
+    def gemm_quant(i):
+        if L.fp8_blockscaled_gemm_quant(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
+                                        vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
+                                        vp(yq.data_ptr()), N, vp(ysc.data_ptr()), accum, hs):
+            raise RuntimeError(fb.last_error())
+
+    def gemm_then_quant(i):
+        if L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
+                                  vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
+                                  vp(y32.data_ptr()), 1, N, accum, hs):
+            raise RuntimeError(fb.last_error())
+        if L.fp8_quant_act_1x128(vp(y32.data_ptr()), 1, M, N, N, 0, vp(yq.data_ptr()), N,
+                                 vp(ysc.data_ptr()), hs):
+            raise RuntimeError(fb.last_error())
+
+    gq_us, g2_us = timed_us(gemm_quant), timed_us(gemm_then_quant)
     dual_us, t128_us, deq_us = timed_us(dual), timed_us(t128x1), timed_us(dequant)
     deq_bytes = M * K * (1 + 2) + 4 * M * (K // 128)
     dual_bytes = M * K * (2 + 1 + 1) + 2 * 4 * M * (K // 128)
@@ -307,6 +329,11 @@ def main():
                                    "GB/s": round(deq_bytes / deq_us / 1e3, 1),
                                    "frac_hbm": round(deq_bytes / deq_us / 1e3 / PEAK_HBM_GBPS, 4),
                                    "bytes": deq_bytes, "launches": 50},
+            "blockscaled_gemm_quant_out": {"accum": args.accum, "avg_us": round(gq_us, 2),
+                                           "TFLOP/s": round(flops / (gq_us * 1e-6) / 1e12, 2),
+                                           "two_launch_us": round(g2_us, 2), "launches": 50,
+                                           "note": "Y quantized 1x128 (E4M3 + scales) in the GEMM "
+                                                   "epilogue vs float32 GEMM then the quantizer"},
             "blockscaled_gemm_other_accum": {
                 "accum": "fp8_mfma" if args.accum == "fp32" else "fp32", "avg_us": round(alt_us, 2),
                 "TFLOP/s": round(flops / (alt_us * 1e-6) / 1e12, 2), "launches": n_alt},

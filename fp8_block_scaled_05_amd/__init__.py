@@ -20,7 +20,7 @@ import re
 
 __all__ = [
     "fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
-    "fp8_blockscaled_gemm",
+    "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant",
     "fp8_blockscaled_grouped_gemm", "last_error", "version", "lib", "lib_path",
     "Fp8bsError", "STATUS",
 ]
@@ -64,9 +64,10 @@ def lib():
     L.fp8_quant_act_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
     L.fp8_dequant.argtypes = [vp, i64, i64, i64, vp, i32, vp, i32, i64, vp]
     L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, i32, vp]
+    L.fp8_blockscaled_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i64, vp, i32, vp]
     L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     for f in ("fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
-              "fp8_blockscaled_gemm", "fp8_blockscaled_grouped_gemm"):
+              "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int
     L.fp8bs_last_error.restype = ctypes.c_char_p
     L.fp8bs_last_error.argtypes = []
@@ -283,6 +284,38 @@ def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=No
                                       _dtype_code(y, "y"), _pitch(y, "y"), _ACCUM[accum],
                                       _stream()))
     return y
+
+
+def fp8_blockscaled_gemm_quant(a, a_scale, b, b_scale, b_kind="block128", yq=None, y_scale=None,
+                               accum="fp32"):
+    """The GEMM with its float32 output quantized in 1x128 tiles by the GEMM's
+    epilogue.  Returns (yq uint8 [M, N], y_scale f32 [M, N/128])."""
+    torch = _torch()
+    _on_gpu(a, a_scale, b, b_scale, yq, y_scale)
+    m, k = a.shape
+    n = b.shape[0]
+    if yq is None:
+        yq = torch.empty((m, n), dtype=torch.uint8, device=a.device)
+    if y_scale is None:
+        y_scale = torch.empty((m, n // 128), dtype=torch.float32, device=a.device)
+    kind = {"block128": BSCALE_BLOCK128, "row": BSCALE_ROW}[b_kind]
+    if b.shape[1] != k:
+        raise ValueError(f"a is [M, {k}] but b is {tuple(b.shape)}")
+    _need(a, (m, k), torch.uint8, "a")
+    _need(b, (n, k), torch.uint8, "b")
+    _need(a_scale, (m, k // 128), torch.float32, "a_scale")
+    _need(b_scale, (n // 128 if kind == BSCALE_BLOCK128 else n, k // 128), torch.float32,
+          "b_scale")
+    _need(yq, (m, n), torch.uint8, "yq")
+    _need(y_scale, (m, n // 128), torch.float32, "y_scale")
+    for t, nm in ((a_scale, "a_scale"), (b_scale, "b_scale"), (y_scale, "y_scale")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    _check(lib().fp8_blockscaled_gemm_quant(m, n, k, _ptr(a), _pitch(a, "a"), _ptr(a_scale),
+                                            _ptr(b), _pitch(b, "b"), _ptr(b_scale), kind,
+                                            _ptr(yq), _pitch(yq, "yq"), _ptr(y_scale),
+                                            _ACCUM[accum], _stream()))
+    return yq, y_scale
 
 
 def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None, y=None,

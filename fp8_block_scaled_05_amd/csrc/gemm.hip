@@ -114,6 +114,7 @@ struct GemmArgs {
   const uint8_t* b;
   const float* b_scale;
   void* y;
+  float* y_scale;           // E4M3 output: [M, N/128] scales of its 1x128 tiles
   const int32_t* off;       // grouped: [G+1] row offsets (device)
   int64_t lda, ldb, ldy;
   int64_t b_group_stride;   // grouped: bytes between experts' B
@@ -224,9 +225,12 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
   return true;
 }
 
-template <bool kBf16Out>
+// Output element types of the GEMM.
+enum OutKind : int { kOutF32 = 0, kOutBf16 = 1, kOutE4M3 = 2 };
+
+template <int kOut>
 __device__ __forceinline__ void store4(void* y, int64_t off, float v0, float v1, float v2, float v3) {
-  if constexpr (kBf16Out) {
+  if constexpr (kOut == kOutBf16) {
     const uint32_t lo = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
     const uint32_t hi = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + off) = make_uint2(lo, hi);
@@ -245,7 +249,7 @@ __device__ __forceinline__ h8 widen8(uint32_t w0, uint32_t w1) {
 }
 
 // ---------------------------------------------------------------------------
-template <class C, bool kF16, bool kRowScale, bool kBf16Out, bool kGrouped>
+template <class C, bool kF16, bool kRowScale, int kOut, bool kGrouped>
 __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) {
   using St = Stage<C::BM, C::BN>;
   using Sg = ScaleGroup<C::BM, C::BN, kRowScale>;
@@ -558,20 +562,82 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
       for (int j = 0; j < SN; ++j) promote(i, j, cprev[i]);
   }
 
-  // Epilogue: four consecutive columns per store.
+  if constexpr (kOut == kOutE4M3) {
+    // Output quantized in 1x128 tiles: the N tile is 128 wide, so each of its
+    // rows is one whole tile.  Row amax over this lane's 32 values, the
+    // partner lane (lane ^ 32) and the other wave column (through LDS); then
+    // s = fl32(amax/448) with the 1e-10 guard and codes of fl32(y/s), the
+    // same operations as the 1x128 quantizer on a float32 input.  Codes go
+    // through an LDS tile (the first stage buffer, free after the main loop;
+    // row pitch 144 bytes) and leave as whole 128-byte rows.
+    static_assert(C::BN == 128, "one 1x128 output tile per row of the N tile");
+    constexpr int kPitch = 144;
+    static_assert(C::BM * kPitch <= int(sizeof(St)), "code tile fits the stage buffer");
+    __shared__ float rmax[C::WN][C::BM];
+    uint8_t* ct = reinterpret_cast<uint8_t*>(&st0);
+    __syncthreads();   // every wave is past its last read of the stages
+    float m[SM];
 #pragma unroll
-  for (int i = 0; i < SM; ++i) {
-    const int64_t row = tile.row0 + arow0 + 32 * i;
-    if (row >= tile.row_end) continue;
+    for (int i = 0; i < SM; ++i) {
+      float v = 0.0f;
 #pragma unroll
-    for (int j = 0; j < SN; ++j)
+      for (int j = 0; j < SN; ++j)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t col = tile.n0 + wn * C::TN + 32 * j + 8 * g + 4 * hk;
-        if (col < args.N)
-          store4<kBf16Out>(args.y, row * args.ldy + col, acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                           acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-      }
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, fabsf(acc[i][j][r]));
+      v = fmaxf(v, __shfl_xor(v, 32));
+      m[i] = v;
+    }
+    if (hk == 0) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i) rmax[wn][arow0 + 32 * i] = m[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int rl = arow0 + 32 * i;
+      float amax = rmax[0][rl];
+#pragma unroll
+      for (int w = 1; w < C::WN; ++w) amax = fmaxf(amax, rmax[w][rl]);
+      const float sc = tile_scale(amax);
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cl = wn * C::TN + 32 * j + 8 * g + 4 * hk;
+          *reinterpret_cast<uint32_t*>(ct + rl * kPitch + cl) =
+              pack4_e4m3(acc[i][j][4 * g] / sc, acc[i][j][4 * g + 1] / sc, acc[i][j][4 * g + 2] / sc,
+                         acc[i][j][4 * g + 3] / sc);
+        }
+      const int64_t row = tile.row0 + rl;
+      if (wn == 0 && hk == 0 && row < tile.row_end)
+        args.y_scale[row * (args.N / 128) + tile.n0 / 128] = sc;
+    }
+    __syncthreads();
+    uint8_t* yq = static_cast<uint8_t*>(args.y);
+#pragma unroll
+    for (int c = threadIdx.x; c < C::BM * 8; c += C::kThreads) {
+      const int rl = c >> 3, ch = c & 7;
+      const int64_t row = tile.row0 + rl;
+      if (row < tile.row_end)
+        *reinterpret_cast<uint4*>(yq + row * args.ldy + tile.n0 + 16 * ch) =
+            *reinterpret_cast<const uint4*>(ct + rl * kPitch + 16 * ch);
+    }
+  } else {
+    // Epilogue: four consecutive columns per store.
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      const int64_t row = tile.row0 + arow0 + 32 * i;
+      if (row >= tile.row_end) continue;
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = tile.n0 + wn * C::TN + 32 * j + 8 * g + 4 * hk;
+          if (col < args.N)
+            store4<kOut>(args.y, row * args.ldy + col, acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                         acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+    }
   }
 }
 
@@ -580,17 +646,20 @@ using CfgLarge = TileCfg<256, 128, 4, 2>;   // 256 x 128 tile, 8 waves of 64 x 6
 using CfgSmall = TileCfg<128, 128, 2, 2>;   // 128 x 128 tile, 4 waves of 64 x 64
 
 template <class C, bool kGrouped>
-void launch_cfg(const GemmArgs& args, bool f16, bool row_scale, bool bf16_out, uint32_t n_wg,
+void launch_cfg(const GemmArgs& args, bool f16, bool row_scale, int out, uint32_t n_wg,
                 hipStream_t stream) {
   const dim3 grid(n_wg), block(C::kThreads);
-#define FP8BS_L(F, R, B) hipLaunchKernelGGL((gemm_kernel<C, F, R, B, kGrouped>), grid, block, 0, stream, args)
+#define FP8BS_L(F, R, O) hipLaunchKernelGGL((gemm_kernel<C, F, R, O, kGrouped>), grid, block, 0, stream, args)
+#define FP8BS_OUT(F, R)                                                    \
+  if (out == kOutBf16) FP8BS_L(F, R, kOutBf16);                            \
+  else if (out == kOutF32) FP8BS_L(F, R, kOutF32);                         \
+  else if constexpr (!kGrouped) FP8BS_L(F, R, kOutE4M3);
   if (f16) {
-    if (row_scale) { if (bf16_out) FP8BS_L(true, true, true); else FP8BS_L(true, true, false); }
-    else { if (bf16_out) FP8BS_L(true, false, true); else FP8BS_L(true, false, false); }
+    if (row_scale) { FP8BS_OUT(true, true) } else { FP8BS_OUT(true, false) }
   } else {
-    if (row_scale) { if (bf16_out) FP8BS_L(false, true, true); else FP8BS_L(false, true, false); }
-    else { if (bf16_out) FP8BS_L(false, false, true); else FP8BS_L(false, false, false); }
+    if (row_scale) { FP8BS_OUT(false, true) } else { FP8BS_OUT(false, false) }
   }
+#undef FP8BS_OUT
 #undef FP8BS_L
 }
 
@@ -605,31 +674,37 @@ bool valid_accum(int32_t accum) { return accum == FP8BS_ACCUM_FP32 || accum == F
 
 using namespace fp8bs;
 
-extern "C" fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a,
-                                             int64_t lda, const float* a_scale, const uint8_t* b,
-                                             int64_t ldb, const float* b_scale, int32_t b_kind,
-                                             void* y, int32_t y_dtype, int64_t ldy, int32_t accum,
-                                             hipStream_t stream) {
-  const char* fn = "fp8_blockscaled_gemm";
+namespace fp8bs {
+namespace {
+
+// Shared by the dense entry points.  `out` is an OutKind; for kOutE4M3, y
+// holds the codes (pitch ldy bytes) and y_scale the [M, N/128] scales.
+fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                        int64_t lda, const float* a_scale, const uint8_t* b, int64_t ldb,
+                        const float* b_scale, int32_t b_kind, void* y, int out, int64_t ldy,
+                        float* y_scale, int32_t accum, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
   if (b_kind != FP8BS_BSCALE_BLOCK128 && b_kind != FP8BS_BSCALE_ROW)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown b_kind %d", fn, b_kind);
-  if (!valid_dtype(y_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
   if (!valid_accum(accum)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown accum %d", fn, accum);
   if (K % 128 || K < 128) return fail(FP8BS_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 128", fn, (long long)K);
   if (b_kind == FP8BS_BSCALE_BLOCK128 && N % 128)
     return fail(FP8BS_ERR_SHAPE, "%s: block128 B scales need N %% 128 == 0 (N=%lld)", fn, (long long)N);
+  if (out == kOutE4M3 && N % 128)
+    return fail(FP8BS_ERR_SHAPE, "%s: 1x128 output tiles need N %% 128 == 0 (N=%lld)", fn, (long long)N);
   if (N % 16) return fail(FP8BS_ERR_SHAPE, "%s: N=%lld must be a multiple of 16", fn, (long long)N);
   if (M == 0 || N == 0) return FP8BS_OK;
-  if (!a || !b || !a_scale || !b_scale || !y) return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
+  if (!a || !b || !a_scale || !b_scale || !y || (out == kOutE4M3 && !y_scale))
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: null pointer", fn);
+  const int64_t y_elt = out == kOutF32 ? 4 : (out == kOutBf16 ? 2 : 1);
   if (lda < K || ldb < K || ldy < N) return fail(FP8BS_ERR_INVALID_ARG, "%s: pitch smaller than the row", fn);
-  if (!aligned16(a) || !aligned16(b) || !aligned16(y) || lda % 16 || ldb % 16 ||
-      (ldy * elem_size(y_dtype)) % 16)
+  if (!aligned16(a) || !aligned16(b) || !aligned16(y) || lda % 16 || ldb % 16 || (ldy * y_elt) % 16)
     return fail(FP8BS_ERR_ALIGNMENT, "%s: operands and row pitches must be 16-byte aligned", fn);
-  if (!aligned4(a_scale) || !aligned4(b_scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
+  if (!aligned4(a_scale) || !aligned4(b_scale) || (y_scale && !aligned4(y_scale)))
+    return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
   if (M > 0x7fffffff || N > 0x7fffffff)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: dimension too large", fn);
-  if (!sane_matrix(M, ldy, elem_size(y_dtype)) || !sane_matrix(M, lda, 1) || !sane_matrix(N, ldb, 1))
+  if (!sane_matrix(M, ldy, int(y_elt)) || !sane_matrix(M, lda, 1) || !sane_matrix(N, ldb, 1))
     return fail(FP8BS_ERR_INVALID_ARG, "%s: sizes and pitches exceed any allocation", fn);
   // Offsets inside one tile are 32-bit: 256 rows of codes or scales.
   if (lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || K / 128 * 256 * 4 > 0x7fffffff)
@@ -637,27 +712,50 @@ extern "C" fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, co
 
   GemmArgs args{};
   args.a = a; args.a_scale = a_scale; args.b = b; args.b_scale = b_scale; args.y = y;
+  args.y_scale = y_scale;
   args.off = nullptr;
   args.lda = lda; args.ldb = ldb; args.ldy = ldy;
   args.M = int32_t(M); args.N = int32_t(N); args.KB = int32_t(K / 128);
   args.G = 1;
   const bool f16 = accum == FP8BS_ACCUM_FP32;
   const bool row = b_kind == FP8BS_BSCALE_ROW;
-  const bool bf16 = y_dtype == FP8BS_BF16;
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 127) / 128);
   if (tiles_large >= kNumCU) {
     args.tiles_m = int32_t((M + 255) / 256);
     args.tiles_n = int32_t((N + 127) / 128);
     const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
     if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgLarge, false>(args, f16, row, bf16, uint32_t(n_wg), stream);
+    launch_cfg<CfgLarge, false>(args, f16, row, out, uint32_t(n_wg), stream);
   } else {
     args.tiles_m = int32_t((M + 127) / 128);
     args.tiles_n = int32_t((N + 127) / 128);
     const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-    launch_cfg<CfgSmall, false>(args, f16, row, bf16, uint32_t(n_wg), stream);
+    launch_cfg<CfgSmall, false>(args, f16, row, out, uint32_t(n_wg), stream);
   }
   return check_launch(fn);
+}
+
+}  // namespace
+}  // namespace fp8bs
+
+extern "C" fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                                             int64_t lda, const float* a_scale, const uint8_t* b,
+                                             int64_t ldb, const float* b_scale, int32_t b_kind,
+                                             void* y, int32_t y_dtype, int64_t ldy, int32_t accum,
+                                             hipStream_t stream) {
+  const char* fn = "fp8_blockscaled_gemm";
+  if (!valid_dtype(y_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
+  return dense_gemm(fn, M, N, K, a, lda, a_scale, b, ldb, b_scale, b_kind, y,
+                    y_dtype == FP8BS_BF16 ? kOutBf16 : kOutF32, ldy, nullptr, accum, stream);
+}
+
+extern "C" fp8bs_status fp8_blockscaled_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                                                   int64_t lda, const float* a_scale, const uint8_t* b,
+                                                   int64_t ldb, const float* b_scale, int32_t b_kind,
+                                                   uint8_t* yq, int64_t ldyq, float* y_scale,
+                                                   int32_t accum, hipStream_t stream) {
+  return dense_gemm("fp8_blockscaled_gemm_quant", M, N, K, a, lda, a_scale, b, ldb, b_scale, b_kind,
+                    yq, kOutE4M3, ldyq, y_scale, accum, stream);
 }
 
 extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t G,
@@ -693,7 +791,7 @@ extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N,
   args.M = int32_t(M_total); args.N = int32_t(N); args.KB = int32_t(K / 128);
   args.G = G;
   const bool f16 = accum == FP8BS_ACCUM_FP32;
-  const bool bf16 = y_dtype == FP8BS_BF16;
+  const int out = y_dtype == FP8BS_BF16 ? kOutBf16 : kOutF32;
   // Upper bound on sum_g ceil(m_g / BM): ceil(M_total / BM) + G.
   const int64_t tiles_large = ((M_total + 255) / 256 + G) * (N / 128);
   if (tiles_large >= 2 * kNumCU) {
@@ -701,13 +799,13 @@ extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N,
     args.tiles_n = int32_t(N / 128);
     const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
     if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgLarge, true>(args, f16, false, bf16, uint32_t(n_wg), stream);
+    launch_cfg<CfgLarge, true>(args, f16, false, out, uint32_t(n_wg), stream);
   } else {
     args.tiles_m = int32_t((M_total + 127) / 128 + G);
     args.tiles_n = int32_t(N / 128);
     const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
     if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgSmall, true>(args, f16, false, bf16, uint32_t(n_wg), stream);
+    launch_cfg<CfgSmall, true>(args, f16, false, out, uint32_t(n_wg), stream);
   }
   return check_launch(fn);
 }

@@ -192,6 +192,28 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
                                   int32_t accum, hipStream_t stream);
 
 /*
+ * The block-scaled GEMM with its output quantized in 1x128 tiles inside the
+ * GEMM's epilogue: the online quantization of the next GEMM's activations
+ * done by their producer (codingmall "Online-kvantisering": each tile's
+ * scale comes from its current values; "Finkornig kvantisering": 1x128
+ * activation tiles).  Every 128-wide output tile of a row is whole inside
+ * one workgroup, so no extra pass over y is needed.
+ *
+ * Same operands, accum and accuracy as fp8_blockscaled_gemm; N % 128 == 0.
+ * The float32 result y[m,n] (the value fp8_blockscaled_gemm would store
+ * with FP8BS_F32) is quantized exactly as fp8_quant_act_1x128 quantizes a
+ * float32 input:
+ *   yq:      [M, N] uint8 codes, pitch ldyq >= N (16-byte aligned);
+ *   y_scale: [M, N/128] float32, s = fl32(amax/448) (1 if not above
+ *            fl32(1e-10)), codes = E4M3_RNE_SAT(fl32(y/s)).
+ */
+fp8bs_status fp8_blockscaled_gemm_quant(int64_t M, int64_t N, int64_t K,
+                                        const uint8_t* a, int64_t lda, const float* a_scale,
+                                        const uint8_t* b, int64_t ldb, const float* b_scale,
+                                        int32_t b_kind, uint8_t* yq, int64_t ldyq,
+                                        float* y_scale, int32_t accum, hipStream_t stream);
+
+/*
  * Grouped (mixture-of-experts) block-scaled GEMM: group g owns rows
  * [off[g], off[g+1]) of a and y and has its own weight b[g]
  * (HolySheep (zh) MoE module: each expert multiplies its own tokens).

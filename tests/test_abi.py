@@ -21,7 +21,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = fb.header_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128",
-                          "fp8_dequant", "fp8_blockscaled_gemm", "fp8_blockscaled_grouped_gemm",
+                          "fp8_dequant", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm",
                           "fp8bs_last_error", "fp8bs_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -128,6 +128,23 @@ def test_gemm_validation(L):
     assert _gemm(L, a=A16 + 8) == ALIGN and _gemm(L, lda=264) == ALIGN
     assert _gemm(L, ydt=0, ldy=260) == ALIGN                            # bf16 pitch 520 B
     assert _gemm(L, sb=A16 + 2) == ALIGN
+
+
+def _gq(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, yq=A16,
+        ldyq=256, ys=A16, accum=0):
+    return L.fp8_blockscaled_gemm_quant(M, N, K, a, lda, sa, b, ldb, sb, kind, yq, ldyq, ys, accum, None)
+
+
+def test_gemm_quant_validation(L):
+    assert _gq(L, M=0) == OK and _gq(L, M=0, yq=NULL, ys=NULL) == OK
+    assert _gq(L, N=144, ldyq=144, kind=1) == SHAPE                     # 1x128 output tiles
+    assert _gq(L, K=64, lda=64, ldb=64) == SHAPE
+    assert _gq(L, ys=NULL) == INVALID and _gq(L, yq=NULL) == INVALID
+    assert _gq(L, kind=3) == INVALID and _gq(L, accum=4) == INVALID
+    assert _gq(L, ldyq=128) == INVALID
+    assert _gq(L, ldyq=264) == ALIGN and _gq(L, yq=A16 + 8) == ALIGN
+    assert _gq(L, ys=A16 + 2) == ALIGN
+    assert _gq(L, ldyq=(1 << 40) + 256) == INVALID
 
 
 def _grouped(L, M=256, N=256, K=256, G=4, off=A16, a=A16, sa=A16, b=A16, sb=A16, y=A16, ydt=0,

@@ -37,37 +37,63 @@ def _check_tol(y, ref, bound, out, what):
 
 
 def _quantize_pair(xbits, wbits):
+    """GPU-side operands: the library's own quantizers."""
     a, sa = fb.fp8_quant_act_1x128(dev_bf16(xbits))
     b, sb, _, _ = fb.fp8_quant_w_128x128(dev_bf16(wbits))
     return a, sa, b, sb
 
 
+def _oracle_pair(xbits, wbits):
+    """Oracle-side operands: the oracle's quantization of the same inputs."""
+    a, sa = oracle.quant_1x128(f32(xbits))
+    b, sb = oracle.quant_128x128(f32(wbits))
+    return a, sa, b, sb
+
+
+def _block_rows(n, count, seed):
+    """`count` seeded 128-row blocks of an N-row weight, first and last included."""
+    nb = n // 128
+    rng = np.random.default_rng(seed)
+    pick = sorted(set([0, nb - 1]) | set(rng.choice(nb, size=min(count, nb), replace=False).tolist()))
+    return pick[:max(count, 2)]
+
+
+def _cols_of(blocks):
+    return np.concatenate([np.arange(128 * bk, 128 * bk + 128) for bk in blocks])
+
+
 # ---------------------------------------------------------------- workloads
 @pytest.mark.parametrize("workload,out", [(1, "f32"), (2, "f32"), (2, "bf16")])
 def test_gemm_full(workload, out):
+    """Whole output; both sides multiply the oracle's quantization of the inputs."""
     d = inputs(workload)
+    a, sa, b, sb = _oracle_pair(d["X"], d["W"])
     banner(f"gemm workload {workload} full, out {out}")
-    a, sa, b, sb = _quantize_pair(d["X"], d["W"])
-    y = fb.fp8_blockscaled_gemm(a, sa, b, sb, "block128",
+    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), "block128",
                                 torch.float32 if out == "f32" else torch.bfloat16)
     torch.cuda.synchronize()
-    ref, bound = oracle.blockscaled_gemm_ref(host(a), host(sa), host(b), host(sb))
+    ref, bound = oracle.blockscaled_gemm_ref(a, sa, b, sb)
     _check_tol(_y_host(y), ref, bound, out, f"workload {workload}")
 
 
-def test_gemm_workload3_sampled_rows():
+def test_gemm_workload3_sampled():
+    """GPU: the library's quantizers feed the GEMM.  Oracle: its own
+    quantization of sampled X rows and whole 128-row blocks of W."""
     d = inputs(3)
-    banner("gemm workload 3 [8192,18432,7168], sampled rows")
+    banner("gemm workload 3 [8192,18432,7168], sampled rows and column blocks")
     a, sa, b, sb = _quantize_pair(d["X"], d["W"])
     y = fb.fp8_blockscaled_gemm(a, sa, b, sb, "block128", torch.float32)
     torch.cuda.synchronize()
-    rows = synth.sample_rows(a.shape[0], 192, seed=3, must=[0, a.shape[0] - 1])
-    ah, sah = host(a)[rows], host(sa)[rows]
-    ref, bound = oracle.blockscaled_gemm_ref(ah, sah, host(b), host(sb))
-    _check_tol(_y_host(y)[rows], ref, bound, "f32", "workload 3")
+    rows = synth.sample_rows(a.shape[0], 128, seed=3, must=[0, a.shape[0] - 1])
+    blocks = _block_rows(b.shape[0], 3, seed=33)
+    cols = _cols_of(blocks)
+    ah, sah = oracle.quant_1x128(f32(d["X"][rows]))
+    bh, sbh = oracle.quant_128x128(f32(d["W"][cols]))
+    ref, bound = oracle.blockscaled_gemm_ref(ah, sah, bh, sbh)
+    _check_tol(_y_host(y)[rows][:, cols], ref, bound, "f32", "workload 3")
 
 
-def test_grouped_workload4_sampled_rows():
+def test_grouped_workload4_sampled():
     d = inputs(4)
     off = d["offsets"]
     g, n, k = d["W"].shape
@@ -79,27 +105,34 @@ def test_grouped_workload4_sampled_rows():
     y = fb.fp8_blockscaled_grouped_gemm(_dev(off), a, sa, b, sb, torch.bfloat16)
     torch.cuda.synchronize()
     must = [int(o) for o in off[:-1] if o < off[-1]] + [int(o) - 1 for o in off[1:] if o > 0]
-    rows = synth.sample_rows(a.shape[0], 160, seed=4, must=must)
+    rows = synth.sample_rows(a.shape[0], 96, seed=4, must=must)
     yh = _y_host(y)
-    ah, sah = host(a), host(sa)
-    bh, sbh = host(b), host(sb)
     expert = np.searchsorted(off, rows, side="right") - 1
+    blocks = _block_rows(n, 2, seed=44)
+    cols = _cols_of(blocks)
     for e in np.unique(expert):
         r = rows[expert == e]
-        ref, bound = oracle.blockscaled_gemm_ref(ah[r], sah[r], bh[e], sbh[e])
-        _check_tol(yh[r], ref, bound, "bf16", f"expert {e}")
+        ah, sah = oracle.quant_1x128(f32(d["X"][r]))
+        bh, sbh = oracle.quant_128x128(f32(d["W"][e][cols]))
+        ref, bound = oracle.blockscaled_gemm_ref(ah, sah, bh, sbh)
+        _check_tol(yh[r][:, cols], ref, bound, "bf16", f"expert {e}")
 
 
 def test_dgrad_workload5():
     d = inputs(5)
-    banner("dgrad workload 5: dY[8192,2048] x W[2048,7168] -> dX, sampled rows")
+    banner("dgrad workload 5: dY[8192,2048] x W[2048,7168] -> dX, sampled rows and columns")
     a, sa = fb.fp8_quant_act_1x128(dev_bf16(d["dY"]))
     _, _, bt, sbt = fb.fp8_quant_w_128x128(dev_bf16(d["W"]), transpose=True)
     y = fb.fp8_blockscaled_gemm(a, sa, bt, sbt, "block128", torch.bfloat16)
     torch.cuda.synchronize()
-    rows = synth.sample_rows(a.shape[0], 256, seed=5, must=[0, a.shape[0] - 1])
-    ref, bound = oracle.blockscaled_gemm_ref(host(a)[rows], host(sa)[rows], host(bt), host(sbt))
-    _check_tol(_y_host(y)[rows], ref, bound, "bf16", "dgrad")
+    rows = synth.sample_rows(a.shape[0], 192, seed=5, must=[0, a.shape[0] - 1])
+    blocks = _block_rows(bt.shape[0], 4, seed=55)           # column blocks of W = rows of W^T
+    cols = _cols_of(blocks)
+    ah, sah = oracle.quant_1x128(f32(d["dY"][rows]))
+    wq, ws = oracle.quant_128x128(f32(d["W"][:, cols]))     # whole 128x128 blocks of W
+    ref, bound = oracle.blockscaled_gemm_ref(ah, sah, np.ascontiguousarray(wq.T),
+                                             np.ascontiguousarray(ws.T))
+    _check_tol(_y_host(y)[rows][:, cols], ref, bound, "bf16", "dgrad")
 
 
 def test_wgrad_workload5():
@@ -109,10 +142,12 @@ def test_wgrad_workload5():
     dyt, sdyt = fb.fp8_quant_act_1x128(dev_bf16(d["dY"]), "128x1_T")  # [2048, 8192]
     y = fb.fp8_blockscaled_gemm(xt, sxt, dyt, sdyt, "row", torch.float32)
     torch.cuda.synchronize()
-    rows = synth.sample_rows(xt.shape[0], 192, seed=55, must=[0, xt.shape[0] - 1])
-    ref, bound = oracle.blockscaled_gemm_ref(host(xt)[rows], host(sxt)[rows], host(dyt),
-                                             host(sdyt), "row")
-    _check_tol(_y_host(y)[rows], ref, bound, "f32", "wgrad")
+    rows = synth.sample_rows(xt.shape[0], 128, seed=55, must=[0, xt.shape[0] - 1])
+    cols = synth.sample_rows(dyt.shape[0], 256, seed=56, must=[0, dyt.shape[0] - 1])
+    ah, sah = oracle.quant_128x1_t(f32(d["X"][:, rows]))
+    bh, sbh = oracle.quant_128x1_t(f32(d["dY"][:, cols]))
+    ref, bound = oracle.blockscaled_gemm_ref(ah, sah, bh, sbh, "row")
+    _check_tol(_y_host(y)[rows][:, cols], ref, bound, "f32", "wgrad")
 
 
 # ---------------------------------------------------------------- exact cases
@@ -181,7 +216,8 @@ def test_scale_routing_powers_of_two():
 def test_tails_and_pitches(m, n, k, kind):
     rng = np.random.default_rng([23, m, n, k])
     x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
-    a, sa = fb.fp8_quant_act_1x128(dev_bf16(x))
+    ah, sah = oracle.quant_1x128(f32(x))
+    a, sa = _dev(ah), _dev(sah)
     b = rng.integers(0, 256, size=(n, k), dtype=np.uint8)
     b[(b & 0x7F) == 0x7F] = 0x38
     sb = (rng.random((n // 128 if kind == "block128" else n, k // 128)) + 0.01).astype(np.float32)
@@ -195,7 +231,7 @@ def test_tails_and_pitches(m, n, k, kind):
     fb.fp8_blockscaled_gemm(abuf[:, :k], sa, bbuf[:, :k], _dev(sb), kind, y=ybuf[1:m + 1, :n])
     torch.cuda.synchronize()
     yb = host(ybuf)
-    ref, bound = oracle.blockscaled_gemm_ref(host(a), host(sa), b, sb, kind)
+    ref, bound = oracle.blockscaled_gemm_ref(ah, sah, b, sb, kind)
     _check_tol(yb[1:m + 1, :n].astype(np.float64), ref, bound, "f32", "tails")
     assert np.all(yb[0] == -3.0) and np.all(yb[-1] == -3.0) and np.all(yb[:, n:] == -3.0)
 
@@ -323,8 +359,7 @@ def test_fp8_mfma_mode_within_group_model(m, n, k, kind):
     d = inputs(1) if (m, k) == (128, 512) else None
     rng = np.random.default_rng([26, m, n, k])
     if d is not None:
-        a, sa, b, sb = _quantize_pair(d["X"], d["W"])
-        a, sa, b, sb = host(a), host(sa), host(b), host(sb)
+        a, sa, b, sb = _oracle_pair(d["X"], d["W"])
     else:
         x = synth.f32_to_bf16_bits(rng.standard_normal((m, k)).astype(np.float32))
         a, sa = oracle.quant_1x128(f32(x))

@@ -1,0 +1,149 @@
+"""GPU checks of the GEMM whose epilogue quantizes its float32 output in 1x128
+tiles (fp8_blockscaled_gemm_quant).
+
+* Where every intermediate is exact in fp32 (integer-valued codes, scales in
+  {1, 2} x {1/2, 1}), the GEMM result equals the oracle's, so codes and scales
+  must equal the oracle's quantization of it bit for bit.
+* On the workloads' data the GEMM result differs from the float64 oracle by up
+  to 2e-5 * sum|a_k b_k|; there the codes are checked against that oracle
+  through bounds that follow from the definition, and nearly all of them must
+  still equal the oracle's codes.
+* The fused result must be the same bytes as quantizing the library's own
+  float32 GEMM output with the 1x128 quantizer (a consistency check between
+  two library paths, not an oracle comparison)."""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_block_scaled_05_amd import synth
+from gpu_util import banner, inputs, host, f32, assert_codes_equal, assert_scales_equal
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+fb = pytest.importorskip("fp8_block_scaled_05_amd")
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _int_codes(rng, shape):
+    """Codes whose values are integers with |v| <= 16."""
+    mags = np.array([0x00, 0x38, 0x40, 0x44, 0x48, 0x4A, 0x4C, 0x4E, 0x50, 0x51, 0x52, 0x53,
+                     0x54, 0x55, 0x56, 0x57, 0x58], np.uint8)          # 0, 1, 2, ..., 16
+    c = mags[rng.integers(0, len(mags), size=shape)]
+    return c | (rng.integers(0, 2, size=shape).astype(np.uint8) << 7)
+
+
+def _exact_case(m, n, k, kind, seed):
+    rng = np.random.default_rng(seed)
+    a = _int_codes(rng, (m, k))
+    b = _int_codes(rng, (n, k))
+    sa = rng.choice(np.float32([1.0, 2.0]), size=(m, k // 128))
+    sb = rng.choice(np.float32([0.5, 1.0]), size=(n // 128 if kind == "block128" else n, k // 128))
+    return a, sa, b, sb
+
+
+@pytest.mark.parametrize("m,n,k,kind,accum", [
+    (300, 256, 1024, "block128", "fp32"),      # small tiles, ragged rows
+    (4096, 2048, 512, "block128", "fp32"),     # large tiles
+    (129, 384, 768, "row", "fp32"),
+    (257, 256, 512, "block128", "fp8_mfma"),   # integer products in one group stay exact there too
+])
+def test_gemm_quant_exact_data_bit_exact(m, n, k, kind, accum):
+    a, sa, b, sb = _exact_case(m, n, k, kind, [40, m, n, k])
+    banner(f"gemm_quant exact data {m}x{n}x{k} {kind} {accum}")
+    yq, ys = fb.fp8_blockscaled_gemm_quant(_dev(a), _dev(sa), _dev(b), _dev(sb), kind, accum=accum)
+    torch.cuda.synchronize()
+    ref, _ = oracle.blockscaled_gemm_ref(a, sa, b, sb, kind)
+    y32 = ref.astype(np.float32)
+    assert np.array_equal(y32.astype(np.float64), ref)                 # exact in fp32
+    want_q, want_s = oracle.quant_1x128(y32)
+    assert_scales_equal(host(ys), want_s, "scale")
+    assert_codes_equal(host(yq), want_q, "codes")
+
+
+def _check_against_oracle(yq, ys, ref, bound):
+    """Codes and scales of a float32 GEMM result within 2e-5*S of ref."""
+    m, n = ref.shape
+    tol = 2e-5 * bound
+    t_ref = np.abs(ref).reshape(m, n // 128, 128)
+    amax = t_ref.max(axis=2)
+    tmax = tol.reshape(m, n // 128, 128).max(axis=2)
+    s = ys.astype(np.float64)
+    guard = s == 1.0
+    err_s = np.abs(448.0 * s - amax)
+    assert np.all(guard | (err_s <= tmax + 2.0 ** -22 * amax)), "scale outside the bound"
+    dq = oracle.e4m3_decode(yq) * np.repeat(s, 128, axis=1)
+    allow = 2.0 * oracle.e4m3_half_ulp(oracle.e4m3_decode(yq)) * np.repeat(s, 128, axis=1)
+    allow += tol + 2.0 ** -23 * np.abs(ref)
+    bad = np.abs(dq - ref) > allow
+    assert not np.any(bad), f"{bad.sum()} codes outside the bound"
+    want_q, _ = oracle.quant_1x128(ref.astype(np.float32))
+    same = np.mean(want_q == yq)
+    assert same >= 0.999, f"only {same:.5f} of codes equal the oracle's"
+
+
+@pytest.mark.parametrize("accum", ["fp32", "fp8_mfma"])
+def test_gemm_quant_workload2_rows(accum):
+    """Workload 2 with the oracle's operand codes on both sides; 512 sampled
+    rows checked against the float64 oracle (fp32 accumulation), the FP8
+    matrix-core mode against its own float32 output."""
+    d = inputs(2)
+    a, sa = oracle.quant_1x128(f32(d["X"]))
+    b, sb = oracle.quant_128x128(f32(d["W"]))
+    banner(f"gemm_quant workload 2 ({accum})")
+    A, SA, B, SB = _dev(a), _dev(sa), _dev(b), _dev(sb)
+    yq, ys = fb.fp8_blockscaled_gemm_quant(A, SA, B, SB, accum=accum)
+    y32 = fb.fp8_blockscaled_gemm(A, SA, B, SB, out_dtype=torch.float32, accum=accum)
+    q2, s2 = fb.fp8_quant_act_1x128(y32)
+    torch.cuda.synchronize()
+    assert torch.equal(yq, q2), "fused codes differ from quantizing the GEMM's float32 output"
+    assert torch.equal(ys.view(torch.int32), s2.view(torch.int32))
+    if accum == "fp32":
+        rows = synth.sample_rows(a.shape[0], 512, seed=41, must=[0, a.shape[0] - 1])
+        ref, bound = oracle.blockscaled_gemm_ref(a[rows], sa[rows], b, sb)
+        _check_against_oracle(host(yq)[rows], host(ys)[rows], ref, bound)
+
+
+def test_gemm_quant_workload1_full():
+    d = inputs(1)
+    a, sa = oracle.quant_1x128(f32(d["X"]))
+    b, sb = oracle.quant_128x128(f32(d["W"]))
+    banner("gemm_quant workload 1")
+    yq, ys = fb.fp8_blockscaled_gemm_quant(_dev(a), _dev(sa), _dev(b), _dev(sb))
+    torch.cuda.synchronize()
+    ref, bound = oracle.blockscaled_gemm_ref(a, sa, b, sb)
+    _check_against_oracle(host(yq), host(ys), ref, bound)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 128, 128), (127, 256, 256), (255, 384, 384), (513, 128, 640)])
+def test_gemm_quant_ragged_rows_pitches_canaries(m, n, k):
+    a, sa, b, sb = _exact_case(m, n, k, "block128", [42, m, n, k])
+    ldq = n + 32
+    qbuf = torch.full((m + 2, ldq), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((m * (n // 128) + 64,), -7.0, dtype=torch.float32, device="cuda")
+    banner(f"gemm_quant ragged {m}x{n}x{k} pitch {ldq}")
+    fb.fp8_blockscaled_gemm_quant(_dev(a), _dev(sa), _dev(b), _dev(sb), yq=qbuf[1:m + 1, :n],
+                                  y_scale=sbuf[32:32 + m * (n // 128)].view(m, n // 128))
+    torch.cuda.synchronize()
+    ref, _ = oracle.blockscaled_gemm_ref(a, sa, b, sb)
+    want_q, want_s = oracle.quant_1x128(ref.astype(np.float32))
+    qb, sbh = host(qbuf), host(sbuf)
+    assert_codes_equal(qb[1:m + 1, :n], want_q, "codes")
+    assert_scales_equal(sbh[32:32 + m * (n // 128)].reshape(m, n // 128), want_s, "scale")
+    assert np.all(qb[0] == 0xA5) and np.all(qb[-1] == 0xA5) and np.all(qb[:, n:] == 0xA5)
+    assert np.all(sbh[:32] == -7.0) and np.all(sbh[32 + m * (n // 128):] == -7.0)
+
+
+def test_gemm_quant_errors():
+    banner("gemm_quant errors")
+    a = torch.zeros((4, 256), dtype=torch.uint8, device="cuda")
+    sa = torch.ones((4, 2), dtype=torch.float32, device="cuda")
+    b = torch.zeros((144, 256), dtype=torch.uint8, device="cuda")
+    sb = torch.ones((144, 2), dtype=torch.float32, device="cuda")
+    with pytest.raises(fb.Fp8bsError):
+        fb.fp8_blockscaled_gemm_quant(a, sa, b, sb, "row")          # N % 128 != 0
+    yq, ys = fb.fp8_blockscaled_gemm_quant(a[:0], sa[:0], b[:128], sb[:128], "row")
+    assert yq.shape == (0, 128) and ys.shape == (0, 1)
