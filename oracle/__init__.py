@@ -32,6 +32,8 @@ from .quantize import (SCALE_GUARD, tile_scale, quant_1x128, quant_128x1_t,
 from .gemm import (blockscaled_gemm_ref, grouped_gemm_ref,
                    blockscaled_gemm_fp32_model, gemm_tolerance_ok)
 from .dequant import dequant_f32, dequant_bf16, f32_to_bf16_rne
+from .e5m2 import E5M2_MAX, e5m2_decode, e5m2_encode, e5m2_magnitudes, e5m2_half_ulp
+from .tensor_scaling import tensor_scale, quant_tensor_current, quant_tensor_delayed
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_magnitudes", "e4m3_half_ulp",
@@ -39,4 +41,6 @@ __all__ = [
     "dequant_1x128", "dequant_128x128",
     "blockscaled_gemm_ref", "grouped_gemm_ref", "blockscaled_gemm_fp32_model",
     "gemm_tolerance_ok", "dequant_f32", "dequant_bf16", "f32_to_bf16_rne",
+    "E5M2_MAX", "e5m2_decode", "e5m2_encode", "e5m2_magnitudes", "e5m2_half_ulp",
+    "tensor_scale", "quant_tensor_current", "quant_tensor_delayed",
 ]

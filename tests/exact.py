@@ -110,3 +110,59 @@ def quantize_tile_exact(values):
         q = rn32(Fraction(x) / Fraction(s))
         codes.append(e4m3_encode_exact(q, neg_zero=math.copysign(1.0, x) < 0))
     return codes, s
+
+
+# E5M2 magnitudes from the bit fields, as exact integers in units of 2^-16:
+# E=0 -> M; E=1..30 -> (4 + M) * 2^(E-1).
+def _e5m2_mag_units(code):
+    e, m = (code >> 2) & 0x1F, code & 3
+    if e == 0:
+        return m
+    return (4 + m) << (e - 1)
+
+
+_E5M2_UNITS = [_e5m2_mag_units(c) for c in range(124)]   # finite codes 0..0x7B
+
+
+def e5m2_value_exact(code):
+    """Fraction value of a finite E5M2 code (None for infinities and NaN)."""
+    if (code >> 2) & 0x1F == 31:
+        return None
+    v = Fraction(_E5M2_UNITS[code & 0x7F], 1 << 16)
+    return -v if code & 0x80 else v
+
+
+def e5m2_encode_exact(v, neg_zero=False):
+    """Nearest E5M2 code of a rational, ties to the even code, saturating at 57344."""
+    v = Fraction(v)
+    neg = v < 0 or (v == 0 and neg_zero)
+    a = abs(v) * (1 << 16)
+    if a >= _E5M2_UNITS[123]:
+        code = 123
+    else:
+        hi = bisect.bisect_left(_E5M2_UNITS, a)
+        if _E5M2_UNITS[hi] == a:
+            code = hi
+        else:
+            lo = hi - 1
+            d_lo, d_hi = a - _E5M2_UNITS[lo], _E5M2_UNITS[hi] - a
+            code = lo if d_lo < d_hi else hi if d_hi < d_lo else (lo if lo % 2 == 0 else hi)
+    return code | (0x80 if neg else 0)
+
+
+def tensor_quantize_exact(values, fmt_max, encode_exact, margin=0.0, amax=None):
+    """Per-tensor scaling by exact arithmetic: each float32 step rounded once.
+
+    s = rn32(rn32(amax * rn32(1 + margin)) / fmt_max), s := 1 if s < rn32(1e-6);
+    codes = encode(rn32(x / s)).  `amax` overrides the tensor's own (delayed).
+    """
+    vals = [float(v) for v in values]
+    if amax is None:
+        amax = max(abs(v) for v in vals)
+    widen = rn32(1 + Fraction(f32_from_bits(f32_bits(margin))))
+    s = rn32(rn32(Fraction(amax) * Fraction(widen)) / fmt_max)
+    if s < rn32(Fraction(1e-6)):
+        s = 1.0
+    codes = [encode_exact(rn32(Fraction(x) / Fraction(s)), neg_zero=math.copysign(1.0, x) < 0)
+             for x in vals]
+    return codes, s
