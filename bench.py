@@ -271,6 +271,24 @@ def main():
                                  vp(ysc.data_ptr()), hs):
             raise RuntimeError(fb.last_error())
 
+    # Prior-art per-tensor scalings on the same X: current (two passes) and
+    # delayed (one pass, 1024-entry amax history).
+    t_scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    t_amax = torch.empty((1,), dtype=torch.float32, device=dev)
+    t_hist = torch.ones((1024,), dtype=torch.float32, device=dev)
+
+    def tensor_current(i):
+        if L.fp8_quant_tensor(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 0, ctypes.c_float(0.0), None, 0,
+                              vp(a.data_ptr()), K, vp(t_scale.data_ptr()), vp(t_amax.data_ptr()), hs):
+            raise RuntimeError(fb.last_error())
+
+    def tensor_delayed(i):
+        if L.fp8_quant_tensor(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 0, ctypes.c_float(0.0),
+                              vp(t_hist.data_ptr()), 1024, vp(a.data_ptr()), K, vp(t_scale.data_ptr()),
+                              vp(t_amax.data_ptr()), hs):
+            raise RuntimeError(fb.last_error())
+
+    tc_us, td_us = timed_us(tensor_current), timed_us(tensor_delayed)
     gq_us, g2_us = timed_us(gemm_quant), timed_us(gemm_then_quant)
     dual_us, t128_us, deq_us = timed_us(dual), timed_us(t128x1), timed_us(dequant)
     deq_bytes = M * K * (1 + 2) + 4 * M * (K // 128)
@@ -329,6 +347,14 @@ def main():
                                    "GB/s": round(deq_bytes / deq_us / 1e3, 1),
                                    "frac_hbm": round(deq_bytes / deq_us / 1e3 / PEAK_HBM_GBPS, 4),
                                    "bytes": deq_bytes, "launches": 50},
+            "quant_tensor_current": {"avg_us": round(tc_us, 2),
+                                     "GB/s": round(M * K * 5 / tc_us / 1e3, 1),
+                                     "bytes": M * K * 5, "launches": 50,
+                                     "note": "per-tensor scale (prior art): amax pass + code pass"},
+            "quant_tensor_delayed": {"avg_us": round(td_us, 2),
+                                     "GB/s": round(M * K * 3 / td_us / 1e3, 1),
+                                     "bytes": M * K * 3, "launches": 50,
+                                     "note": "per-tensor scale from a 1024-entry amax history"},
             "blockscaled_gemm_quant_out": {"accum": args.accum, "avg_us": round(gq_us, 2),
                                            "TFLOP/s": round(flops / (gq_us * 1e-6) / 1e12, 2),
                                            "two_launch_us": round(g2_us, 2), "launches": 50,

@@ -20,6 +20,7 @@ import re
 
 __all__ = [
     "fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
+    "fp8_quant_tensor",
     "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant",
     "fp8_blockscaled_grouped_gemm", "last_error", "version", "lib", "lib_path",
     "Fp8bsError", "STATUS",
@@ -33,6 +34,8 @@ BF16, F32 = 0, 1
 TILE_1x128, TILE_128x1_T, TILE_128x128 = 0, 1, 2
 BSCALE_BLOCK128, BSCALE_ROW = 0, 1
 ACCUM_FP32, ACCUM_FP8_MFMA = 0, 1
+FMT_E4M3, FMT_E5M2 = 0, 1
+_FMT = {"e4m3": FMT_E4M3, "e5m2": FMT_E5M2}
 _ACCUM = {"fp32": ACCUM_FP32, "fp8_mfma": ACCUM_FP8_MFMA}
 
 
@@ -63,10 +66,13 @@ def lib():
     L.fp8_quant_w_128x128.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
     L.fp8_quant_act_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
     L.fp8_dequant.argtypes = [vp, i64, i64, i64, vp, i32, vp, i32, i64, vp]
+    L.fp8_quant_tensor.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_float, vp, i32, vp, i64,
+                                   vp, vp, vp]
     L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, i32, vp]
     L.fp8_blockscaled_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i64, vp, i32, vp]
     L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp]
     for f in ("fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
+              "fp8_quant_tensor",
               "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int
     L.fp8bs_last_error.restype = ctypes.c_char_p
@@ -251,6 +257,35 @@ def fp8_dequant(q, scale, tiling="1x128", out_dtype=None, y=None):
     _check(lib().fp8_dequant(_ptr(q), rows, cols, _pitch(q, "q"), _ptr(scale), tcode, _ptr(y),
                              _dtype_code(y, "y"), _pitch(y, "y"), _stream()))
     return y
+
+
+def fp8_quant_tensor(x, fmt="e4m3", margin=0.0, history=None, q=None, scale=None, amax=None):
+    """Per-tensor quantization (the prior-art baselines).  history None:
+    current scaling from max|x|; history (float32 [L] on the GPU): delayed
+    scaling from max(history), which is then updated in place.
+    Returns (q uint8 like x, scale f32 [1], amax f32 [1])."""
+    torch = _torch()
+    _on_gpu(x, history, q, scale, amax)
+    rows, cols = x.shape
+    dev = x.device
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    if amax is None:
+        amax = torch.empty((1,), dtype=torch.float32, device=dev)
+    _need(q, (rows, cols), torch.uint8, "q")
+    _need(scale, (1,), torch.float32, "scale")
+    _need(amax, (1,), torch.float32, "amax")
+    hl = 0
+    if history is not None:
+        if history.dtype != torch.float32 or history.dim() != 1 or not history.is_contiguous():
+            raise ValueError("history must be a contiguous float32 vector")
+        hl = history.numel()
+    _check(lib().fp8_quant_tensor(_ptr(x), _dtype_code(x, "x"), rows, cols, _pitch(x, "x"),
+                                  _FMT[fmt], float(margin), _ptr(history), hl, _ptr(q),
+                                  _pitch(q, "q"), _ptr(scale), _ptr(amax), _stream()))
+    return q, scale, amax
 
 
 def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None,

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libfp8bs.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["status.cpp", "quant.hip", "dequant.hip", "gemm.hip"]
+SOURCES = ["status.cpp", "quant.hip", "dequant.hip", "tensor_quant.hip", "gemm.hip"]
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the generated code.
 # Division and sqrt stay correctly rounded (hipcc's default); no fast-math.

@@ -65,6 +65,11 @@ typedef enum fp8bs_act_tiling {
   FP8BS_TILE_128x128 = 2       /* 128x128 blocks (weights); accepted by fp8_dequant */
 } fp8bs_act_tiling;
 
+typedef enum fp8bs_format {
+  FP8BS_FMT_E4M3 = 0,          /* OCP E4M3FN, max 448 */
+  FP8BS_FMT_E5M2 = 1           /* OCP E5M2, max 57344 (per-tensor baselines only) */
+} fp8bs_format;
+
 typedef enum fp8bs_bscale_kind {
   FP8BS_BSCALE_BLOCK128 = 0,   /* b_scale[N/128][K/128]: one scale per 128x128 block of B */
   FP8BS_BSCALE_ROW = 1         /* b_scale[N][K/128]: one scale per row of B and 128-K block */
@@ -165,6 +170,38 @@ fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64_t rows, in
 fp8bs_status fp8_dequant(const uint8_t* q, int64_t rows, int64_t cols, int64_t ld_q,
                          const float* scale, int32_t tiling, void* y, int32_t y_dtype,
                          int64_t ldy, hipStream_t stream);
+
+/*
+ * Per-tensor quantization: the prior-art scalings that the fine-grained
+ * tiles are compared with (one scale for the whole tensor).
+ *
+ * Current scaling (history == NULL), HolySheep (zh) troubleshooting entry
+ * on FP8 overflow, SafeFP8Quantizer.safe_quantize:
+ *   amax = max|x|;  s = fl32(fl32(amax * fl32(1 + margin)) / fmt_max);
+ *   s = 1 if s < fl32(1e-6);  code = SAT(RNE(fl32(x / s))).
+ *   Two passes over x (amax, then the codes).
+ * Delayed scaling (history != NULL), HolySheep (zh) FP8Config
+ *   (amax_history_len 1024, margin 0): the same formula with amax replaced
+ *   by max(history[0 .. history_len)), the amaxes of earlier calls; codes
+ *   saturate at the format maximum (a stale scale can be too small); then
+ *   history becomes [max|x|, history[0 .. history_len-2]].  One pass.
+ *
+ * format:  fp8bs_format.  E5M2 is the hybrid recipe's gradient format
+ *          (German HolySheep article); DeepSeek-V3 uses E4M3 throughout
+ *          (codingmall "Unified E4M3 Format").
+ * x:       [rows, cols] of x_dtype, pitch ld_x >= cols; cols % 8 == 0.
+ * q:       [rows, cols] uint8 codes, pitch ld_q >= cols.
+ * scale:   DEVICE float[1]: the dequantizing scale s used.
+ * amax:    DEVICE float[1]: max|x| of this call (also the reduction's
+ *          accumulator).
+ * history: DEVICE float[history_len] (1..4096) or NULL; updated in place.
+ * margin:  >= 0.  Zero rows or columns: nothing is written (the history is
+ *          unchanged).  Inputs must be finite.
+ */
+fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
+                              int64_t ld_x, int32_t format, float margin, float* history,
+                              int32_t history_len, uint8_t* q, int64_t ld_q, float* scale,
+                              float* amax, hipStream_t stream);
 
 /*
  * Block-scaled FP8 GEMM with FP32 promotion per 128-deep K block

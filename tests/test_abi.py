@@ -21,7 +21,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = fb.header_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128",
-                          "fp8_dequant", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm",
+                          "fp8_dequant", "fp8_quant_tensor", "fp8_blockscaled_gemm",
+                          "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm",
                           "fp8bs_last_error", "fp8bs_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -106,6 +107,24 @@ def test_dequant_validation(L):
     assert _deq(L, ldq=392) == ALIGN and _deq(L, ydt=0, ldy=388) == ALIGN   # 776 B bf16 rows
     assert _deq(L, s=A16 + 2) == ALIGN
     assert _deq(L, ldq=(1 << 40) + 384) == INVALID
+
+
+def _tq(L, x=A16, dt=0, rows=4, cols=64, ldx=64, fmt=0, margin=0.0, h=NULL, hl=0, q=A16, ldq=64,
+        s=A4, a=A4):
+    return L.fp8_quant_tensor(x, dt, rows, cols, ldx, fmt, margin, h, hl, q, ldq, s, a, None)
+
+
+def test_quant_tensor_validation(L):
+    assert _tq(L, rows=0) == OK and _tq(L, rows=0, x=NULL, q=NULL, s=NULL, a=NULL) == OK
+    assert _tq(L, fmt=2) == INVALID and _tq(L, dt=3) == INVALID
+    assert _tq(L, margin=-0.1) == INVALID and _tq(L, margin=float("nan")) == INVALID
+    assert _tq(L, h=A4, hl=0) == INVALID and _tq(L, h=A4, hl=5000) == INVALID
+    assert _tq(L, cols=60, ldx=64, ldq=64) == SHAPE
+    assert _tq(L, s=NULL) == INVALID and _tq(L, a=NULL) == INVALID and _tq(L, q=NULL) == INVALID
+    assert _tq(L, ldx=56) == INVALID and _tq(L, ldq=56) == INVALID
+    assert _tq(L, x=A16 + 4) == ALIGN and _tq(L, ldq=72) == ALIGN and _tq(L, ldx=68) == ALIGN
+    assert _tq(L, s=A4 + 1) == ALIGN and _tq(L, h=A4 + 2, hl=8) == ALIGN
+    assert _tq(L, ldx=(1 << 40) + 64) == INVALID
 
 
 def _gemm(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, y=A16,
