@@ -254,6 +254,9 @@ constexpr int kCPitch = 132;  // bytes
 #ifndef FP8BS_DUAL_GRID
 #define FP8BS_DUAL_GRID 65536
 #endif
+#ifndef FP8BS_T_VIA_BLOCKS
+#define FP8BS_T_VIA_BLOCKS 1
+#endif
 
 __device__ __forceinline__ void transpose4x4_bytes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
                                                    uint32_t& o0, uint32_t& o1, uint32_t& o2,
@@ -417,7 +420,9 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
 // The next block's input is loaded into registers while the current one is
 // processed.  Three barriers per block; the LDS buffers written after each
 // one were last read before the previous one.
-template <bool kBf16, int kThreads>
+// kRowOut false: only the 128x1 output (the 128x1_T tiling of
+// fp8_quant_act_1x128 when cols is a multiple of 128).
+template <bool kBf16, int kThreads, bool kRowOut>
 __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __restrict__ x, int64_t ld_x,
                                                               int64_t rows, int64_t cols,
                                                               uint8_t* __restrict__ q, int64_t ld_q,
@@ -458,13 +463,15 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
     for (int p = 0; p < kRows; ++p) unpack8<kBf16>(cur.d[p], v[p]);
 
     // 1x128 tiles.
+    if constexpr (kRowOut) {
 #pragma unroll
-    for (int p = 0; p < kRows; ++p) {
-      const float s = tile_scale(row16_max(absmax8(v[p])));
-      const float r = 1.0f / s;
-      const int64_t row = r0 + rbase + kRowStep * p;
-      store_codes8(q + row * ld_q + c0 + cc, encode8<kBf16>(v[p], s, r));
-      if ((t & 15) == 0) store_scale(&scale[row * row_kb + bj], s);
+      for (int p = 0; p < kRows; ++p) {
+        const float s = tile_scale(row16_max(absmax8(v[p])));
+        const float r = 1.0f / s;
+        const int64_t row = r0 + rbase + kRowStep * p;
+        store_codes8(q + row * ld_q + c0 + cc, encode8<kBf16>(v[p], s, r));
+        if ((t & 15) == 0) store_scale(&scale[row * row_kb + bj], s);
+      }
     }
 
     // 128x1 tiles: column maxima.
@@ -587,6 +594,19 @@ extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int6
     else
       hipLaunchKernelGGL((quant_1x128_kernel<false, kActU>), grid, dim3(256), 0, stream, x, ld_x,
                          static_cast<uint32_t>(n_tiles), per_row, q, ld_q, scale);
+  } else if (cols % 128 == 0 && FP8BS_T_VIA_BLOCKS) {
+    // Whole 128x128 blocks: the dual kernel without its row output.
+    const int64_t n_blocks = (rows / 128) * (cols / 128);
+    if (n_blocks > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many blocks", fn);
+    const int64_t per_wg = (n_blocks + FP8BS_DUAL_GRID - 1) / FP8BS_DUAL_GRID;
+    const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
+    constexpr int kT = FP8BS_DUAL_THREADS;
+    if (bf16)
+      hipLaunchKernelGGL((quant_dual_kernel<true, kT, false>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols,
+                         nullptr, int64_t(0), nullptr, q, ld_q, scale);
+    else
+      hipLaunchKernelGGL((quant_dual_kernel<false, kT, false>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols,
+                         nullptr, int64_t(0), nullptr, q, ld_q, scale);
   } else {
     if ((cols + 63) / 64 > 0x7fffffff || rows / 128 > 65535)
       return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles for the launch grid", fn);
@@ -664,8 +684,8 @@ extern "C" fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64
   const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
   constexpr int kT = FP8BS_DUAL_THREADS;
   if (x_dtype == FP8BS_BF16)
-    hipLaunchKernelGGL((quant_dual_kernel<true, kT>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+    hipLaunchKernelGGL((quant_dual_kernel<true, kT, true>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   else
-    hipLaunchKernelGGL((quant_dual_kernel<false, kT>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+    hipLaunchKernelGGL((quant_dual_kernel<false, kT, true>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
   return check_launch(fn);
 }
