@@ -95,8 +95,12 @@ __global__ __launch_bounds__(64) void fill_kernel(float* p, float v) {
 
 // Chunk c (8 elements) is row c / (cols / 8), columns 8 (c % (cols / 8)) ...
 // Each thread takes kU chunks per pass of its grid-stride loop (chunks
-// 256 u + t of a 256 kU block), all loads issued before their use.
+// kTT u + t of a kTT kU block), all loads issued before their use.
 constexpr int kTU = 4;
+// One workgroup of 1024 threads per CU: at most 256 amax atomics per call,
+// and 16 waves x 4 chunks of loads in flight per CU.
+constexpr int kTT = 1024;
+constexpr int kTGrid = 256;
 
 template <bool kBf16>
 __device__ __forceinline__ const char* chunk_ptr(const void* x, int64_t ld_x, FastDiv per_row, uint32_t c,
@@ -107,16 +111,16 @@ __device__ __forceinline__ const char* chunk_ptr(const void* x, int64_t ld_x, Fa
 }
 
 template <bool kBf16>
-__global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict__ x, int64_t ld_x,
+__global__ __launch_bounds__(kTT) void tensor_amax_kernel(const void* __restrict__ x, int64_t ld_x,
                                                           uint32_t n_chunks, FastDiv per_row,
                                                           float* __restrict__ amax) {
-  __shared__ float red[4];
+  __shared__ float red[kTT / 64];
   float m = 0.0f;
-  for (uint32_t base = blockIdx.x * 256u * kTU; base < n_chunks; base += gridDim.x * 256u * kTU) {
+  for (uint32_t base = blockIdx.x * kTT * kTU; base < n_chunks; base += gridDim.x * kTT * kTU) {
     float v[kTU][8];
 #pragma unroll
     for (int u = 0; u < kTU; ++u) {
-      uint32_t c = base + 256u * u + threadIdx.x, row, col;
+      uint32_t c = base + kTT * u + threadIdx.x, row, col;
       c = c < n_chunks ? c : n_chunks - 1;        // repeats a chunk: harmless for a maximum
       load8t<kBf16>(chunk_ptr<kBf16>(x, ld_x, per_row, c, row, col), v[u]);
     }
@@ -136,18 +140,18 @@ __global__ __launch_bounds__(256) void tensor_amax_kernel(const void* __restrict
 // wherever the code is not zero; a stale delayed scale can make x / s
 // overflow, so the delayed kernel divides (IEEE) and saturates.
 template <bool kBf16, bool kE5M2, bool kDelayed>
-__global__ __launch_bounds__(256) void tensor_quant_kernel(const void* __restrict__ x, int64_t ld_x,
+__global__ __launch_bounds__(kTT) void tensor_quant_kernel(const void* __restrict__ x, int64_t ld_x,
                                                            uint32_t n_chunks, FastDiv per_row,
                                                            const float* __restrict__ src, int hist_len,
                                                            float widen, uint8_t* __restrict__ q,
                                                            int64_t ld_q, float* __restrict__ scale_out,
                                                            float* __restrict__ amax_out) {
-  __shared__ float red[4];
+  __shared__ float red[kTT / 64];
   constexpr float kMax = kE5M2 ? kE5M2Max : kE4M3Max;
   float ref;
   if constexpr (kDelayed) {
     float h = 0.0f;
-    for (int i = threadIdx.x; i < hist_len; i += 256) h = fmaxf(h, src[i]);
+    for (int i = threadIdx.x; i < hist_len; i += kTT) h = fmaxf(h, src[i]);
     ref = block_max(h, red);
   } else {
     ref = src[0];
@@ -157,18 +161,18 @@ __global__ __launch_bounds__(256) void tensor_quant_kernel(const void* __restric
   if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = s;
   float m = 0.0f;
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  for (uint32_t base = blockIdx.x * 256u * kTU; base < n_chunks; base += gridDim.x * 256u * kTU) {
+  for (uint32_t base = blockIdx.x * kTT * kTU; base < n_chunks; base += gridDim.x * kTT * kTU) {
     float v[kTU][8];
     uint32_t row[kTU], col[kTU];
 #pragma unroll
     for (int u = 0; u < kTU; ++u) {
-      uint32_t c = base + 256u * u + threadIdx.x;
+      uint32_t c = base + kTT * u + threadIdx.x;
       c = c < n_chunks ? c : n_chunks - 1;
       load8t<kBf16>(chunk_ptr<kBf16>(x, ld_x, per_row, c, row[u], col[u]), v[u]);
     }
 #pragma unroll
     for (int u = 0; u < kTU; ++u) {
-      if (base + 256u * u + threadIdx.x >= n_chunks) break;
+      if (base + kTT * u + threadIdx.x >= n_chunks) break;
       float w[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -242,24 +246,23 @@ extern "C" fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t
   const int64_t n_chunks = rows * per_row;
   if (n_chunks > 0xf0000000LL) return fail(FP8BS_ERR_INVALID_ARG, "%s: more than 2^32 chunks", fn);
   const FastDiv div(static_cast<uint32_t>(per_row));
-  // A grid-stride loop over at most 1024 workgroups (one amax atomic each at most).
-  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((n_chunks + 256 * kTU - 1) / (256 * kTU), 1024));
+  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((n_chunks + kTT * kTU - 1) / (kTT * kTU), kTGrid));
   const float widen = 1.0f + margin;
   const bool bf16 = x_dtype == FP8BS_BF16, e5 = format == FP8BS_FMT_E5M2;
 
   hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(64), 0, stream, amax, 0.0f);
 #define FP8BS_Q(B, E, D, SRC, L)                                                                 \
-  hipLaunchKernelGGL((tensor_quant_kernel<B, E, D>), dim3(grid), dim3(256), 0, stream, x, ld_x, \
+  hipLaunchKernelGGL((tensor_quant_kernel<B, E, D>), dim3(grid), dim3(kTT), 0, stream, x, ld_x, \
                      static_cast<uint32_t>(n_chunks), div, SRC, L, widen, q, ld_q, scale, amax)
 #define FP8BS_Q2(D, SRC, L)                                                                       \
   if (bf16) { if (e5) FP8BS_Q(true, true, D, SRC, L); else FP8BS_Q(true, false, D, SRC, L); }    \
   else { if (e5) FP8BS_Q(false, true, D, SRC, L); else FP8BS_Q(false, false, D, SRC, L); }
   if (!history) {
     if (bf16)
-      hipLaunchKernelGGL((tensor_amax_kernel<true>), dim3(grid), dim3(256), 0, stream, x, ld_x,
+      hipLaunchKernelGGL((tensor_amax_kernel<true>), dim3(grid), dim3(kTT), 0, stream, x, ld_x,
                          static_cast<uint32_t>(n_chunks), div, amax);
     else
-      hipLaunchKernelGGL((tensor_amax_kernel<false>), dim3(grid), dim3(256), 0, stream, x, ld_x,
+      hipLaunchKernelGGL((tensor_amax_kernel<false>), dim3(grid), dim3(kTT), 0, stream, x, ld_x,
                          static_cast<uint32_t>(n_chunks), div, amax);
     FP8BS_Q2(false, amax, 0)
   } else {
