@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=M,
                    help="rows of X in the oracle's timed sample (default: all)")
+    p.add_argument("--extra-workloads", action="store_true",
+                   help="also time the GEMMs (and quantizers) of the other workload shapes: dense FFN, "
+                        "MoE grouped, dgrad and wgrad (reported under extra_workloads)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one device copy of 128 MiB (counter calibration for rocprofv3 --pmc)")
     return p.parse_args()
@@ -93,6 +96,89 @@ def cpu_baseline(xbits, wbits, rows):
                        f"{dt:.2f} s wall; quantizer single-threaded numpy, GEMM on "
                        f"{blas_threads} BLAS threads"),
             "seconds": round(dt, 3)}
+
+
+def extra_workloads(L, fb, torch, dev, hs, accum):
+    """Time each other workload's kernels on operands of its exact shapes.
+
+    Codes are uniform random E4M3 bytes without NaN, scales uniform in
+    [0.5, 1.5), generated on the GPU (the values do not change the work);
+    the MoE expert counts are the workload's seeded counts.  Each kernel is
+    timed over back-to-back launches with events on the launch stream."""
+    from fp8_block_scaled_05_amd import synth
+    vp = ctypes.c_void_p
+
+    def codes(*shape):
+        return torch.randint(0, 0x7E, shape, dtype=torch.uint8, device=dev)
+
+    def scales(*shape):
+        return torch.rand(shape, device=dev) + 0.5
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(torch.cuda.current_stream())
+        for _ in range(n):
+            fn()
+        t1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n * 1e3
+
+    def check(st):
+        if st:
+            raise RuntimeError(fb.last_error())
+
+    out = {}
+
+    def dense(name, m, n, k, kind, ydt, iters):
+        a, sa, b = codes(m, k), scales(m, k // 128), codes(n, k)
+        sb = scales(n // 128, k // 128) if kind == 0 else scales(n, k // 128)
+        y = torch.empty((m, n), dtype=torch.bfloat16 if ydt == 0 else torch.float32, device=dev)
+        us = timed(lambda: check(L.fp8_blockscaled_gemm(m, n, k, vp(a.data_ptr()), k, vp(sa.data_ptr()),
+                                                        vp(b.data_ptr()), k, vp(sb.data_ptr()), kind,
+                                                        vp(y.data_ptr()), ydt, n, accum, hs)), iters)
+        out[name] = {"M": m, "N": n, "K": k, "b_scales": "block128" if kind == 0 else "row",
+                     "out": "bf16" if ydt == 0 else "f32", "avg_us": round(us, 2),
+                     "TFLOP/s": round(2 * m * n * k / us / 1e6, 2)}
+
+    dense("ffn_8192x18432x7168", 8192, 18432, 7168, 0, 0, 10)
+    dense("dgrad_8192x7168x2048", 8192, 7168, 2048, 0, 0, 20)
+    dense("wgrad_7168x2048x8192", 7168, 2048, 8192, 1, 1, 20)
+
+    counts = synth.expert_counts()
+    off_h = synth.offsets_from_counts(counts)
+    m, n, k, g = int(off_h[-1]), 4096, 7168, len(counts)
+    off = torch.from_numpy(off_h).to(dev)
+    a, sa = codes(m, k), scales(m, k // 128)
+    b, sb = codes(g, n, k), scales(g, n // 128, k // 128)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    us = timed(lambda: check(L.fp8_blockscaled_grouped_gemm(m, n, k, g, vp(off.data_ptr()), vp(a.data_ptr()),
+                                                            vp(sa.data_ptr()), vp(b.data_ptr()),
+                                                            vp(sb.data_ptr()), vp(y.data_ptr()), 0, accum,
+                                                            hs)), 5)
+    out["moe_grouped_32768x4096x7168_g16"] = {"M_total": m, "N": n, "K": k, "G": g,
+                                              "counts": counts.tolist(), "avg_us": round(us, 2),
+                                              "TFLOP/s": round(2 * m * n * k / us / 1e6, 2)}
+    del a, b, y
+    # The MoE workload's quantizers: X [32768, 7168] 1x128, the 16 expert
+    # weights as one [65536, 7168] 128x128 call.
+    x = torch.randn((m, k), device=dev).to(torch.bfloat16)
+    q, s1 = torch.empty((m, k), dtype=torch.uint8, device=dev), torch.empty((m, k // 128), device=dev)
+    us = timed(lambda: check(L.fp8_quant_act_1x128(vp(x.data_ptr()), 0, m, k, k, 0, vp(q.data_ptr()), k,
+                                                   vp(s1.data_ptr()), hs)), 10)
+    byt = m * k * 3 + 4 * m * (k // 128)
+    out["quant_act_1x128_32768x7168"] = {"avg_us": round(us, 2), "GB/s": round(byt / us / 1e3, 1),
+                                         "frac_hbm": round(byt / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    del x, q, s1
+    w = (torch.randn((g * n, k), device=dev) * 0.02).to(torch.bfloat16)
+    q, s2 = torch.empty((g * n, k), dtype=torch.uint8, device=dev), torch.empty((g * n // 128, k // 128), device=dev)
+    us = timed(lambda: check(L.fp8_quant_w_128x128(vp(w.data_ptr()), 0, g * n, k, k, vp(q.data_ptr()), k,
+                                                   vp(s2.data_ptr()), None, 0, None, hs)), 10)
+    byt = g * n * k * 3 + 4 * (g * n // 128) * (k // 128)
+    out["quant_w_128x128_65536x7168"] = {"avg_us": round(us, 2), "GB/s": round(byt / us / 1e3, 1),
+                                         "frac_hbm": round(byt / us / 1e3 / PEAK_HBM_GBPS, 4)}
+    return out
 
 
 def main():
@@ -365,6 +451,9 @@ def main():
                 "TFLOP/s": round(flops / (alt_us * 1e-6) / 1e12, 2), "launches": n_alt},
         },
     }
+    if args.extra_workloads:
+        print("[bench] timing the other workload shapes", file=sys.stderr, flush=True)
+        result["extra_workloads"] = extra_workloads(L, fb, torch, dev, hs, accum)
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xbits, wbits, args.cpu_rows)
