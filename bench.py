@@ -36,8 +36,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "170c1c827b8f20c400b16b0089f971da3de61fbecae92175634aa7d7700492b3",
-           "bytes_per_launch": 137163276,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.81 MB written
+TRAFFIC = {"gemm_sha256": "424bf14dcfadc9ef73846946a7c4d2e665021d18597a03020a3a0a6787b70b04",
+           "bytes_per_launch": 137158395,   # 120.36 MB read (FETCH_SIZE x 1.99941) + 16.79 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 

@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "device.hpp"
 #include "fp8bs.h"
@@ -124,9 +125,13 @@ struct GemmArgs {
   int32_t G;
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+// kStages: LDS stages in the K-block ring (2 or 3).  kMinWaves: waves per
+// SIMD the register budget must allow (2 keeps a wave at 256 registers, so
+// that two 4-wave workgroups share a CU).
+template <int BM_, int BN_, int WM_, int WN_, int kStages_ = 3, int kMinWaves_ = 1>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int kStages = kStages_, kMinWaves = kMinWaves_;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -250,10 +255,13 @@ __device__ __forceinline__ h8 widen8(uint32_t w0, uint32_t w1) {
 
 // ---------------------------------------------------------------------------
 template <class C, bool kF16, bool kRowScale, int kOut, bool kGrouped>
-__global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) {
+__global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const GemmArgs args) {
   using St = Stage<C::BM, C::BN>;
   using Sg = ScaleGroup<C::BM, C::BN, kRowScale>;
-  __shared__ St st0, st1, st2;
+  struct NoStage { uint8_t unused[16]; };
+  using St3 = typename std::conditional<C::kStages == 3, St, NoStage>::type;
+  __shared__ St st0, st1;
+  __shared__ St3 st2;
   __shared__ Sg sg[2];
   constexpr int SM = C::SM, SN = C::SN, NW = C::kWaves;
 
@@ -447,7 +455,9 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
   // read of stage s is issued before the barrier, which is what lets the
   // next step refill it.  The scales are read after it: their group buffer
   // is refilled only two steps later.
-  auto step = [&](const St& s, const St& nxt, int kb, float sbv, int mode) {
+  // after_barrier runs right after the block's barrier (the 2-stage ring
+  // issues its loads there, into the stage just released).
+  auto step = [&](const St& s, const St& nxt, int kb, float sbv, int mode, auto&& after_barrier) {
     const Sg& scl = sg[(kb >> 2) & 1];
     // The scheduling fences keep the compiler from hoisting later slices'
     // reads and widening ahead of the current slice's matrix work, which
@@ -466,6 +476,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
     }
     if (mode == 1) wait_and_barrier<kLoadsPerStage>();
     else if (mode == 2) wait_and_barrier<0>();
+    after_barrier();
     if (mode != 0) {
       if constexpr (kF16) read_slice(nxt, 0, 0);
       else read_slice8(nxt, 0, 0);
@@ -502,6 +513,34 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
     }
   };
 
+  if constexpr (C::kStages == 2) {
+    // Two-stage ring: block kb is in stage kb % 2.  The barrier of step kb
+    // (before its last slice) waits for block kb + 1 and, since every read of
+    // stage kb % 2 precedes it, releases that stage: block kb + 2 is loaded
+    // into it right after the barrier, one step ahead of its use.  Scale
+    // group g + 1 is loaded after the barrier of step 4 g + 1; its buffer
+    // held group g - 1, last read by step 4 g - 1.
+    load_scales(0);
+    load_stage(st0, 0);
+    wait_and_barrier<0>();
+    if (KB > 1) load_stage(st1, 1);
+    if constexpr (kF16) read_slice(st0, 0, 0);
+    else read_slice8(st0, 0, 0);
+#define FP8BS_STEP2(CUR, NXT, KBV)                                              \
+    if ((KBV) < KB) {                                                           \
+      const int kb_ = (KBV);                                                    \
+      const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                        \
+      step(CUR, NXT, kb_, sbv_, kb_ + 1 < KB ? 2 : 0, [&] {                     \
+        if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);        \
+        if (kb_ + 2 < KB) load_stage(CUR, kb_ + 2);                             \
+      });                                                                       \
+    }
+    for (int kb = 0; kb < KB; kb += 2) {
+      FP8BS_STEP2(st0, st1, kb)
+      FP8BS_STEP2(st1, st0, kb + 1)
+    }
+#undef FP8BS_STEP2
+  } else {
   // Prologue: scales of K blocks 0..3 and K blocks 0 and 1 in flight,
   // block 0 visible, its slice 0 read.
   load_scales(0);
@@ -532,7 +571,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
     if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     load_stage(FUT, kb_ + 2);                                             \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(CUR, NXT, kb_, sbv_, 1);                                         \
+    step(CUR, NXT, kb_, sbv_, 1, [] {});                                  \
   }
 #define FP8BS_STEP_TAIL(CUR, NXT, FUT, KBV)                                \
   if ((KBV) < KB) {                                                       \
@@ -540,7 +579,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
     if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     if (kb_ + 2 < KB) load_stage(FUT, kb_ + 2);                           \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(CUR, NXT, kb_, sbv_, kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2)); \
+    step(CUR, NXT, kb_, sbv_, kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2), [] {}); \
   }
   int kb = 0;
   for (; kb + 4 < KB; kb += 3) {
@@ -554,6 +593,7 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
   FP8BS_STEP_TAIL(st0, st1, st2, kb + 3)
 #undef FP8BS_STEP_FULL
 #undef FP8BS_STEP_TAIL
+  }
 
   if constexpr (kLag) {
 #pragma unroll
@@ -644,6 +684,11 @@ __global__ __launch_bounds__(C::kThreads) void gemm_kernel(const GemmArgs args) 
 // ---------------------------------------------------------------------------
 using CfgLarge = TileCfg<256, 128, 4, 2>;   // 256 x 128 tile, 8 waves of 64 x 64
 using CfgSmall = TileCfg<128, 128, 2, 2>;   // 128 x 128 tile, 4 waves of 64 x 64
+// 128 x 128 tile, 4 waves of 64 x 64, two LDS stages: two workgroups share a
+// CU and keep their own barriers.  Used for per-row B scales, whose
+// promotion needs a scale product per accumulator: the 256 x 128 tile
+// spills there (~40 registers) and this one does not.
+using CfgPair = TileCfg<128, 128, 2, 2, 2, 2>;
 
 template <class C, bool kGrouped>
 void launch_cfg(const GemmArgs& args, bool f16, bool row_scale, int out, uint32_t n_wg,
@@ -720,7 +765,13 @@ fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const u
   const bool f16 = accum == FP8BS_ACCUM_FP32;
   const bool row = b_kind == FP8BS_BSCALE_ROW;
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 127) / 128);
-  if (tiles_large >= kNumCU) {
+  if (row && tiles_large >= kNumCU) {
+    args.tiles_m = int32_t((M + 127) / 128);
+    args.tiles_n = int32_t((N + 127) / 128);
+    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
+    launch_cfg<CfgPair, false>(args, f16, row, out, uint32_t(n_wg), stream);
+  } else if (tiles_large >= kNumCU) {
     args.tiles_m = int32_t((M + 255) / 256);
     args.tiles_n = int32_t((N + 127) / 128);
     const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;

@@ -161,7 +161,9 @@ def _int_codes(rng, shape):
 
 @pytest.mark.parametrize("m,n,k,kind,out", [(256, 256, 7168, "block128", "f32"),
                                             (300, 384, 1024, "row", "f32"),
-                                            (129, 128, 128, "block128", "f32")])
+                                            (129, 128, 128, "block128", "f32"),
+                                            (4096, 2048, 1024, "row", "f32"),   # paired 128x128 tiles
+                                            (4000, 2064, 640, "row", "f32")])   # paired, ragged M and N
 def test_integer_exact_is_bit_exact(m, n, k, kind, out):
     rng = np.random.default_rng([20, m, n, k])
     a = _int_codes(rng, (m, k))

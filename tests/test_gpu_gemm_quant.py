@@ -49,6 +49,7 @@ def _exact_case(m, n, k, kind, seed):
     (300, 256, 1024, "block128", "fp32"),      # small tiles, ragged rows
     (4096, 2048, 512, "block128", "fp32"),     # large tiles
     (129, 384, 768, "row", "fp32"),
+    (4096, 2048, 768, "row", "fp32"),          # paired 128x128 tiles, two LDS stages
     (257, 256, 512, "block128", "fp8_mfma"),   # integer products in one group stay exact there too
 ])
 def test_gemm_quant_exact_data_bit_exact(m, n, k, kind, accum):
