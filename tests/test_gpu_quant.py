@@ -1,7 +1,6 @@
 """GPU parity of the quantizers against the CPU oracle: codes and scales must be
 bit-exact, on the five workloads (full or on row/column/block samples the
 oracle can compute) and on edge cases."""
-import os
 
 import numpy as np
 import pytest
