@@ -36,8 +36,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "424bf14dcfadc9ef73846946a7c4d2e665021d18597a03020a3a0a6787b70b04",
-           "bytes_per_launch": 137158395,   # 120.36 MB read (FETCH_SIZE x 1.99941) + 16.79 MB written
+TRAFFIC = {"gemm_sha256": "bdcb902977f484cd632cae7d910003d085ee8e2bbdda4315d518c914641f850d",
+           "bytes_per_launch": 137160298,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.80 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
@@ -96,6 +96,23 @@ def cpu_baseline(xbits, wbits, rows):
                        f"{dt:.2f} s wall; quantizer single-threaded numpy, GEMM on "
                        f"{blas_threads} BLAS threads"),
             "seconds": round(dt, 3)}
+
+
+def device_info(torch):
+    """Name, compute units and clocks of cuda:0 (clocks from rocm-smi if present)."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", None),
+            "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+        clk = [l.split(":", 1)[-1].strip() for l in out.splitlines() if "sclk" in l.lower() or "mclk" in l.lower()]
+        if clk:
+            info["clocks_at_exit"] = clk[:4]
+    except Exception:  # noqa: BLE001 - rocm-smi is optional
+        pass
+    return info
 
 
 def extra_workloads(L, fb, torch, dev, hs, accum):
@@ -280,6 +297,7 @@ def main():
     per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev])
     avg_ms = per.mean(axis=0)
     med_ms = np.median(per, axis=0)
+    min_ms = per.min(axis=0)
     qx_bytes, qw_bytes, flops = algorithmic()
     gemm_tflops = flops / (avg_ms[2] * 1e-3) / 1e12
     peak = PEAK_F16_TFLOPS if args.accum == "fp32" else PEAK_FP8_TFLOPS
@@ -418,20 +436,24 @@ def main():
                                "128x128, GEMM Y[4096,2048] with FP32 promotion per 128-K block",
                    "M": M, "N": N, "K": K, "out": args.out, "accum": args.accum,
                    "buffer_sets": n_sets},
+        "device": device_info(torch),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
                      "traffic": traffic},
         "kernels": {
             "quant_act_1x128": {"avg_us": round(avg_ms[0] * 1e3, 2), "median_us": round(med_ms[0] * 1e3, 2),
+                                "min_us": round(min_ms[0] * 1e3, 2),
                                 "GB/s": round(qx_gbps, 1), "frac_hbm": round(qx_gbps / PEAK_HBM_GBPS, 4),
                                 "bytes": qx_bytes, "back_to_back_us": round(qx_b2b_us, 2),
                                 "back_to_back_frac_hbm": round(qx_bytes / qx_b2b_us / 1e3 / PEAK_HBM_GBPS, 4)},
             "quant_w_128x128": {"avg_us": round(avg_ms[1] * 1e3, 2), "median_us": round(med_ms[1] * 1e3, 2),
+                                "min_us": round(min_ms[1] * 1e3, 2),
                                 "GB/s": round(qw_gbps, 1), "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4),
                                 "bytes": qw_bytes, "back_to_back_us": round(qw_b2b_us, 2),
                                 "back_to_back_frac_hbm": round(qw_bytes / qw_b2b_us / 1e3 / PEAK_HBM_GBPS, 4)},
             "blockscaled_gemm": {"accum": args.accum, "mfma": "f16" if args.accum == "fp32" else "fp8",
                                  "avg_us": round(avg_ms[2] * 1e3, 2), "median_us": round(med_ms[2] * 1e3, 2),
+                                 "min_us": round(min_ms[2] * 1e3, 2),
                                  "TFLOP/s": round(gemm_tflops, 2),
                                  "frac_own_peak": round(gemm_tflops / peak, 4),
                                  "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "flops": flops},

@@ -52,10 +52,6 @@
 #include "fp8bs.h"
 #include "status.hpp"
 
-#ifndef FP8BS_LAG
-#define FP8BS_LAG 0
-#endif
-
 namespace fp8bs {
 
 namespace {
@@ -345,24 +341,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     b_off[q] = lds_off(brow0, 4 * hk + q);
   }
 
-  // Block partials.  With the block-128 B scales the promotion is lagged by
-  // one K block: the partials of block kb stay in p and are promoted at the
-  // start of step kb + 1, subtile by subtile just before that subtile's first
-  // matrix instruction, so the FMAs issue while the matrix core works on the
-  // other subtiles.  cprev holds their per-row factors sa * sb.
-  constexpr bool kLag = !kRowScale && FP8BS_LAG;
+  // Block partials P_kb of the wave's subtiles, promoted into acc at the end
+  // of each step.
   v16f p[SM][SN];
-  float cprev[SM];
-  if constexpr (kLag) {
-#pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      cprev[i] = 0.0f;
-#pragma unroll
-      for (int j = 0; j < SN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[i][j][r] = 0.0f;
-    }
-  }
   auto promote = [&](int i, int j, float c) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[i][j][r], c, acc[i][j][r]);
@@ -412,17 +393,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 #pragma unroll
         for (int j = 0; j < SN; ++j) {
           if (q == 0 && t == 0) {
-            // Promote the previous block's partial of this subtile, then
-            // start the new one in the same registers; the fences keep the
-            // compiler from overlapping the two (which would need 16 more
-            // registers per subtile).
-            if constexpr (kLag) {
-              promote(i, j, cprev[i]);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-            const v16f z = {};
+            const v16f z = {};   // a new block's partial starts from zero
             p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], z, 0, 0, 0);
-            if constexpr (kLag) __builtin_amdgcn_sched_barrier(0);
           } else {
             p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], p[i][j], 0, 0, 0);
           }
@@ -437,12 +409,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
         if (qq == 0) {
-          if constexpr (kLag) {
-            promote(i, j, cprev[i]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
           p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[0][j], fa8[0][i], v16f{}, 0, 0, 0, 0, 0, 0);
-          if constexpr (kLag) __builtin_amdgcn_sched_barrier(0);
         } else {
           p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[1][j], fa8[1][i], p[i][j], 0, 0, 0, 0, 0, 0);
         }
@@ -490,10 +457,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     float ca[SM];
 #pragma unroll
     for (int i = 0; i < SM; ++i) ca[i] = scl.sa[arow0 + 32 * i][kb & 3];
-    if constexpr (kLag) {
-#pragma unroll
-      for (int i = 0; i < SM; ++i) cprev[i] = ca[i] * sbv;
-    } else if constexpr (!kRowScale) {
+    if constexpr (!kRowScale) {
 #pragma unroll
       for (int i = 0; i < SM; ++i) {
         const float c = ca[i] * sbv;
@@ -593,13 +557,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   FP8BS_STEP_TAIL(st0, st1, st2, kb + 3)
 #undef FP8BS_STEP_FULL
 #undef FP8BS_STEP_TAIL
-  }
-
-  if constexpr (kLag) {
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-      for (int j = 0; j < SN; ++j) promote(i, j, cprev[i]);
   }
 
   if constexpr (kOut == kOutE4M3) {
