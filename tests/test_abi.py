@@ -203,3 +203,31 @@ def test_binding_raises_typed_error():
     with pytest.raises(fb.Fp8bsError) as e:
         fb._check(2)
     assert e.value.status == 2
+
+
+def test_header_is_plain_c_and_links_from_c(tmp_path):
+    """fp8bs.h compiles as C99 and C++17, and a C program linked against the
+    library gets the documented statuses (validation only: no GPU needed)."""
+    import os
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("gcc not found")
+    here = os.path.dirname(os.path.abspath(__file__))
+    inc = os.path.join(os.path.dirname(here), "include")
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    flags = ["-D__HIP_PLATFORM_AMD__", "-I", inc, "-I", os.path.join(rocm, "include")]
+    src = os.path.join(here, "c_abi_check.c")
+    exe = str(tmp_path / "c_abi_check")
+    lib_dir = os.path.dirname(fb.lib_path())
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Wextra", "-Werror", *flags, src, "-o", exe,
+                        "-L", lib_dir, "-lfp8bs", "-Wl,-rpath," + lib_dir], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r2 = subprocess.run([shutil.which("g++") or "g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only",
+                         "-x", "c++", *flags, src], capture_output=True, text=True)
+    assert r2.returncode == 0, r2.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert "0 failure(s)" in run.stdout
+
