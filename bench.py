@@ -11,7 +11,9 @@ cycled and the 256 MB Infinity Cache cannot serve repeated reads.
 Prints one JSON line.  `value` is whole-step throughput in TFLOP/s
 (2*M*N*K per step over the measured step time, quantization included); the
 `roofline` object covers the dominant kernel (the GEMM) with its average
-launch duration from HIP events recorded on the stream the kernels run on;
+launch duration from HIP events recorded on the stream the kernels run on,
+around each kernel of every 8th timed step (events on every step would add
+~10 us of their own to each step's time);
 `kernels` gives the same for each kernel, the quantizers as GB/s against HBM;
 `cpu_baseline` times the CPU oracle on a bounded sample of the same step.
 """
@@ -58,6 +60,8 @@ def parse():
     p.add_argument("--out", choices=["bf16", "f32"], default="bf16")
     p.add_argument("--accum", choices=["fp32", "fp8_mfma"], default="fp32",
                    help="block-partial accumulation of the GEMM (see include/fp8bs.h)")
+    p.add_argument("--event-every", type=int, default=8,
+                   help="record per-kernel events on every Nth timed step (1 = every step)")
     p.add_argument("--rotate-mib", type=int, default=1100,
                    help="bytes of input/output buffers cycled through (defeats the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,34 +271,47 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps, events around each kernel on the launch stream.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: K steps.  Every event_every-th step also records events
+    # around each of its kernels on the launch stream (the per-kernel and
+    # roofline timings); recording them on every step would add ~10 us of
+    # event overhead to each step's time.
+    # (The first sampled step is not the first timed step, which follows the
+    # synchronization and starts cold.)
+    sampled = [i for i in range(args.steps) if i % args.event_every == args.event_every // 2]
+    if not sampled:
+        sampled = [args.steps - 1]
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def mark(e, k):
+        if e is not None:
+            e[k].record(stream)
+
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
         j = i % n_sets
-        e = ev[i]
-        e[0].record(stream)
+        e = ev.get(i)
+        mark(e, 0)
         if L.fp8_quant_act_1x128(vp(xs[j].data_ptr()), 0, M, K, K, 0, vp(a.data_ptr()), K,
                                  vp(sa.data_ptr()), hs):
             raise RuntimeError(fb.last_error())
-        e[1].record(stream)
+        mark(e, 1)
         if L.fp8_quant_w_128x128(vp(ws[j].data_ptr()), 0, N, K, K, vp(b.data_ptr()), K,
                                  vp(sb.data_ptr()), None, 0, None, hs):
             raise RuntimeError(fb.last_error())
-        e[2].record(stream)
+        mark(e, 2)
         if L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
                                   vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
                                   vp(ys[j].data_ptr()), ycode, N, accum, hs):
             raise RuntimeError(fb.last_error())
-        e[3].record(stream)
+        mark(e, 3)
     end.record(stream)
     torch.cuda.synchronize()
 
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
-    per = np.array([[e[k].elapsed_time(e[k + 1]) for k in range(3)] for e in ev])
+    per = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in sampled])
     avg_ms = per.mean(axis=0)
     med_ms = np.median(per, axis=0)
     min_ms = per.min(axis=0)
@@ -435,7 +452,7 @@ def main():
         "config": {"workload": "linear layer: quantize X[4096,7168] 1x128 + W[2048,7168] "
                                "128x128, GEMM Y[4096,2048] with FP32 promotion per 128-K block",
                    "M": M, "N": N, "K": K, "out": args.out, "accum": args.accum,
-                   "buffer_sets": n_sets},
+                   "buffer_sets": n_sets, "kernel_event_steps": len(sampled)},
         "device": device_info(torch),
         "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
