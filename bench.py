@@ -38,8 +38,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "bdcb902977f484cd632cae7d910003d085ee8e2bbdda4315d518c914641f850d",
-           "bytes_per_launch": 137160298,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.80 MB written
+TRAFFIC = {"gemm_sha256": "4d00c59884255a9720f9274b43e6b7221b98d1912f5730a17773841f31663841",
+           "bytes_per_launch": 137150403,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.79 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
@@ -103,19 +103,26 @@ def cpu_baseline(xbits, wbits, rows):
 
 
 def device_info(torch):
-    """Name, compute units and clocks of cuda:0 (clocks from rocm-smi if present)."""
-    import subprocess
+    """Name, compute units and current clock levels of cuda:0.
+
+    The clocks are read from the driver's sysfs files; no other program is
+    started, since a child process started after the GPU is initialised
+    (e.g. under a profiler's preload) must not exec another program."""
+    import glob
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", None),
             "compute_units": p.multi_processor_count,
             "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-        clk = [l.split(":", 1)[-1].strip() for l in out.splitlines() if "sclk" in l.lower() or "mclk" in l.lower()]
-        if clk:
-            info["clocks_at_exit"] = clk[:4]
-    except Exception:  # noqa: BLE001 - rocm-smi is optional
-        pass
+    for kind in ("sclk", "mclk"):
+        for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
+            try:
+                with open(path) as f:
+                    cur = [l.split(":", 1)[-1].strip(" *\n") for l in f if l.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                info[f"{kind}_at_exit"] = cur[0]
+                break
     return info
 
 

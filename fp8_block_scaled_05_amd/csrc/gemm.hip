@@ -240,6 +240,9 @@ __device__ __forceinline__ void store4(void* y, int64_t off, float v0, float v1,
   }
 }
 
+// Makes x live in registers here: values feeding it must be computed first.
+__device__ __forceinline__ void keep_in_vgprs(v16f& x) { asm volatile("" : "+v"(x)); }
+
 // 8 E4M3 codes (two words) -> 8 f16 values (exact).
 __device__ __forceinline__ h8 widen8(uint32_t w0, uint32_t w1) {
   const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
@@ -341,12 +344,46 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     b_off[q] = lds_off(brow0, 4 * hk + q);
   }
 
-  // Block partials P_kb of the wave's subtiles, promoted into acc at the end
-  // of each step.
-  v16f p[SM][SN];
-  auto promote = [&](int i, int j, float c) {
+  // Block partials P_kb of the wave's subtiles.  On the f16 path with
+  // block-128 B scales (kLag), a block may be left pending in one of two
+  // buffers and promoted during the next block's first two operand slices,
+  // two subtiles per slice, so its FMAs issue between that block's matrix
+  // instructions rather than in one run after the barrier, where both waves
+  // of a SIMD would reach them together and leave the matrix core idle.
+  // (Finishing before the slice after the barrier keeps the kernel within
+  // the register budget without spills.)  Which blocks are
+  // deferred is fixed per unrolled step (see the main loops).  Otherwise
+  // (FP8 path, per-row B scales) p[0] holds every block and is promoted at
+  // the end of its step.  Either way each accumulator receives the same FMAs
+  // in the same order.
+  constexpr bool kLag = kF16 && !kRowScale;
+  v16f p[2][SM][SN];
+  float cl[SM];   // kLag: sa * sb of the pending block
+  if constexpr (kLag) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[i][j][r], c, acc[i][j][r]);
+    for (int i = 0; i < SM; ++i) {
+      cl[i] = 0.0f;   // nothing is pending before block 0: acc += 0 * 0
+#pragma unroll
+      for (int j = 0; j < SN; ++j) p[1][i][j] = v16f{};
+    }
+  }
+  auto promote = [&](auto par_c, int i, int j, float c) {
+    constexpr int par = decltype(par_c)::value;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[par][i][j][r], c, acc[i][j][r]);
+  };
+  // kLag: the pending block's subtiles s = i * SN + j with s / 2 == q.  The
+  // empty asm makes the updated accumulators live at this point, so the
+  // compiler cannot sink these FMAs into a later run.
+  static_assert(!kLag || SM * SN <= 4, "the pending block is promoted in slices 0 and 1");
+  auto promote_lagged = [&](auto par_c, int q) {
+    constexpr int prev = decltype(par_c)::value ^ 1;
+#pragma unroll
+    for (int s = 0; s < SM * SN; ++s)
+      if (s / 2 == q) {
+        promote(std::integral_constant<int, prev>{}, s / SN, s % SN, cl[s / SN]);
+        keep_in_vgprs(acc[s / SN][s % SN]);
+      }
   };
 
   // Operand fragments, carried across steps.  f16 path: raw E4M3 slices of
@@ -378,7 +415,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     }
   };
   // f16 path: widen slice q and run its two k-steps.
-  auto mma_slice = [&](int q, int buf) {
+  auto mma_slice = [&](auto par_c, int q, int buf) {
+    constexpr int par = decltype(par_c)::value;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       h8 fa[SM], fb[SN];
@@ -394,9 +432,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
         for (int j = 0; j < SN; ++j) {
           if (q == 0 && t == 0) {
             const v16f z = {};   // a new block's partial starts from zero
-            p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], z, 0, 0, 0);
+            p[par][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], z, 0, 0, 0);
           } else {
-            p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], p[i][j], 0, 0, 0);
+            p[par][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], p[par][i][j], 0, 0, 0);
           }
         }
     }
@@ -409,9 +447,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
         if (qq == 0) {
-          p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[0][j], fa8[0][i], v16f{}, 0, 0, 0, 0, 0, 0);
+          p[0][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[0][j], fa8[0][i], v16f{}, 0, 0, 0, 0, 0, 0);
         } else {
-          p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[1][j], fa8[1][i], p[i][j], 0, 0, 0, 0, 0, 0);
+          p[0][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb8[1][j], fa8[1][i], p[0][i][j], 0, 0, 0, 0, 0, 0);
         }
       }
   };
@@ -424,7 +462,16 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   // is refilled only two steps later.
   // after_barrier runs right after the block's barrier (the 2-stage ring
   // issues its loads there, into the stage just released).
-  auto step = [&](const St& s, const St& nxt, int kb, float sbv, int mode, auto&& after_barrier) {
+  // The lag arguments are std::integral_constant (p[] is indexed
+  // statically) and matter only with kLag: par_c, the buffer this block
+  // accumulates into; in_c, promote the pending block of the other buffer
+  // during this one; keep_c, leave this block pending (else it is promoted
+  // at the end of the step).
+  auto step = [&](auto par_c, auto in_c, auto keep_c, const St& s, const St& nxt, int kb, float sbv,
+                  int mode, auto&& after_barrier) {
+    using Par = std::integral_constant<int, kLag ? decltype(par_c)::value : 0>;
+    constexpr bool kIn = kLag && decltype(in_c)::value;
+    constexpr bool kKeep = kLag && decltype(keep_c)::value;
     const Sg& scl = sg[(kb >> 2) & 1];
     // The scheduling fences keep the compiler from hoisting later slices'
     // reads and widening ahead of the current slice's matrix work, which
@@ -433,7 +480,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
         read_slice(s, q + 1, (q + 1) & 1);
-        mma_slice(q, q & 1);
+        mma_slice(Par{}, q, q & 1);
+        if constexpr (kIn) promote_lagged(Par{}, q);
         __builtin_amdgcn_sched_barrier(0);
       }
     } else {
@@ -448,8 +496,12 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
       if constexpr (kF16) read_slice(nxt, 0, 0);
       else read_slice8(nxt, 0, 0);
     }
-    if constexpr (kF16) mma_slice(3, 1);
-    else mma_slice8(1);
+    if constexpr (kF16) {
+      mma_slice(Par{}, 3, 1);
+      if constexpr (kIn) promote_lagged(Par{}, 3);
+    } else {
+      mma_slice8(1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // Promotion.  Accumulator r of subtile (i, j) is output row
@@ -457,12 +509,17 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     float ca[SM];
 #pragma unroll
     for (int i = 0; i < SM; ++i) ca[i] = scl.sa[arow0 + 32 * i][kb & 3];
-    if constexpr (!kRowScale) {
+    if constexpr (kKeep) {
+      // This block waits in p[Par]; the next step (or the end of the loop)
+      // promotes it with these products.
+#pragma unroll
+      for (int i = 0; i < SM; ++i) cl[i] = ca[i] * sbv;
+    } else if constexpr (!kRowScale) {
 #pragma unroll
       for (int i = 0; i < SM; ++i) {
         const float c = ca[i] * sbv;
 #pragma unroll
-        for (int j = 0; j < SN; ++j) promote(i, j, c);
+        for (int j = 0; j < SN; ++j) promote(Par{}, i, j, c);
       }
     } else {
 #pragma unroll
@@ -472,7 +529,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
           const float sbn = scl.sb[wn * C::TN + 32 * j + 8 * (r >> 2) + 4 * hk + (r & 3)][kb & 3];
 #pragma unroll
           for (int i = 0; i < SM; ++i)
-            acc[i][j][r] = __builtin_fmaf(p[i][j][r], ca[i] * sbn, acc[i][j][r]);
+            acc[i][j][r] = __builtin_fmaf(p[0][i][j][r], ca[i] * sbn, acc[i][j][r]);
         }
     }
   };
@@ -490,18 +547,20 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     if (KB > 1) load_stage(st1, 1);
     if constexpr (kF16) read_slice(st0, 0, 0);
     else read_slice8(st0, 0, 0);
-#define FP8BS_STEP2(CUR, NXT, KBV)                                              \
+#define FP8BS_STEP2(PAR, CUR, NXT, KBV)                                         \
     if ((KBV) < KB) {                                                           \
       const int kb_ = (KBV);                                                    \
       const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                        \
-      step(CUR, NXT, kb_, sbv_, kb_ + 1 < KB ? 2 : 0, [&] {                     \
+      step(std::integral_constant<int, (PAR)>{}, std::true_type{},              \
+           std::true_type{}, CUR, NXT, kb_, sbv_,                               \
+           kb_ + 1 < KB ? 2 : 0, [&] {                                          \
         if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);        \
         if (kb_ + 2 < KB) load_stage(CUR, kb_ + 2);                             \
       });                                                                       \
     }
     for (int kb = 0; kb < KB; kb += 2) {
-      FP8BS_STEP2(st0, st1, kb)
-      FP8BS_STEP2(st1, st0, kb + 1)
+      FP8BS_STEP2(0, st0, st1, kb)
+      FP8BS_STEP2(1, st1, st0, kb + 1)
     }
 #undef FP8BS_STEP2
   } else {
@@ -529,34 +588,65 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   // already covers it; its buffer held group g - 1, last read in step
   // 4 g - 1, which every wave has finished once it passes the barrier of
   // step 4 g.
-#define FP8BS_STEP_FULL(CUR, NXT, FUT, KBV)                                \
+#define FP8BS_STEP_FULL(KIND, CUR, NXT, FUT, KBV)                          \
   {                                                                       \
     const int kb_ = (KBV);                                                \
     if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     load_stage(FUT, kb_ + 2);                                             \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(CUR, NXT, kb_, sbv_, 1, [] {});                                  \
+    step(KIND##_PAR{}, KIND##_IN{}, KIND##_KEEP{}, CUR, NXT, kb_, sbv_, 1, [] {}); \
   }
-#define FP8BS_STEP_TAIL(CUR, NXT, FUT, KBV)                                \
+#define FP8BS_STEP_TAIL(KIND, CUR, NXT, FUT, KBV)                          \
   if ((KBV) < KB) {                                                       \
     const int kb_ = (KBV);                                                \
     if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     if (kb_ + 2 < KB) load_stage(FUT, kb_ + 2);                           \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(CUR, NXT, kb_, sbv_, kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2), [] {}); \
+    step(KIND##_PAR{}, KIND##_IN{}, KIND##_KEEP{}, CUR, NXT, kb_, sbv_,   \
+         kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2), [] {});               \
   }
+  // With kLag, blocks 3 j, 3 j + 1, 3 j + 2 are steps of kinds A, B, C:
+  // A accumulates into p[0] and stays pending; B promotes it while
+  // accumulating into p[1], which stays pending; C promotes that while
+  // accumulating into p[0] and promotes its own block at its end.  So no
+  // block is pending across iterations, and two promotions in three overlap
+  // matrix work.  (Alternating all blocks would need a six-block loop,
+  // whose code the compiler cannot fit in the register budget.)
+  using A_PAR = std::integral_constant<int, 0>;
+  using A_IN = std::false_type;
+  using A_KEEP = std::true_type;
+  using B_PAR = std::integral_constant<int, 1>;
+  using B_IN = std::true_type;
+  using B_KEEP = std::true_type;
+  using C_PAR = std::integral_constant<int, 0>;
+  using C_IN = std::true_type;
+  using C_KEEP = std::false_type;
   int kb = 0;
   for (; kb + 4 < KB; kb += 3) {
-    FP8BS_STEP_FULL(st0, st1, st2, kb)
-    FP8BS_STEP_FULL(st1, st2, st0, kb + 1)
-    FP8BS_STEP_FULL(st2, st0, st1, kb + 2)
+    FP8BS_STEP_FULL(A, st0, st1, st2, kb)
+    FP8BS_STEP_FULL(B, st1, st2, st0, kb + 1)
+    FP8BS_STEP_FULL(C, st2, st0, st1, kb + 2)
   }
-  FP8BS_STEP_TAIL(st0, st1, st2, kb)
-  FP8BS_STEP_TAIL(st1, st2, st0, kb + 1)
-  FP8BS_STEP_TAIL(st2, st0, st1, kb + 2)
-  FP8BS_STEP_TAIL(st0, st1, st2, kb + 3)
+  FP8BS_STEP_TAIL(A, st0, st1, st2, kb)
+  FP8BS_STEP_TAIL(B, st1, st2, st0, kb + 1)
+  FP8BS_STEP_TAIL(C, st2, st0, st1, kb + 2)
+  FP8BS_STEP_TAIL(A, st0, st1, st2, kb + 3)
 #undef FP8BS_STEP_FULL
 #undef FP8BS_STEP_TAIL
+  }
+
+  // kLag: the last block, K block KB - 1, may still be pending: in
+  // p[(KB - 1) & 1] on the two-stage ring; on the three-stage ring in p[0]
+  // after an A step and in p[1] after a B step.
+  if constexpr (kLag) {
+    const int last = C::kStages == 2 ? ((KB - 1) & 1) : ((KB - 1) % 3);
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) {
+        if (last == 1) promote(std::integral_constant<int, 1>{}, i, j, cl[i]);
+        else if (last == 0) promote(std::integral_constant<int, 0>{}, i, j, cl[i]);
+      }
   }
 
   if constexpr (kOut == kOutE4M3) {
