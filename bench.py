@@ -38,7 +38,7 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "4d00c59884255a9720f9274b43e6b7221b98d1912f5730a17773841f31663841",
+TRAFFIC = {"gemm_sha256": "bf2bb704b82b4f124c35481356a083c6252597abd4fcd9bbf3d206674b32dd83",
            "bytes_per_launch": 137150403,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.79 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20

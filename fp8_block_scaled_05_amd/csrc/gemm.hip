@@ -28,8 +28,9 @@
 //
 // Structure (dense 256 x 128 output tile, 8 waves of 64 x 64):
 //  * A three-stage LDS ring.  Each stage holds one K block of the A and B
-//    tiles (128 bytes per row) and that block's scales, filled by 16-byte
-//    direct global->LDS buffer loads issued two blocks ahead.  Buffer
+//    tiles (128 bytes per row), filled by 16-byte direct global->LDS buffer
+//    loads issued two blocks ahead; the scales follow in groups of four K
+//    blocks, double-buffered.  Buffer
 //    addressing returns zeros for rows past the end of A (or of a group) and
 //    past N, so tails need no branches.  Each stage lives in its own LDS
 //    object so the compiler can track which loads a read depends on.
@@ -40,7 +41,9 @@
 //    its second, so a lane's accumulators share one output row (m) per 32-row
 //    subtile and the promotion needs one sa*sb product per subtile.
 //  * Promotion: one FP32 FMA per output element per K block (two with the
-//    per-row B scales of the weight-gradient GEMM).
+//    per-row B scales of the weight-gradient GEMM).  With block-128 B
+//    scales, two blocks in three are promoted during the next block's
+//    matrix work instead of after it (see the main loop).
 //  * Workgroups are renumbered so that each XCD (own L2) works on a compact
 //    block of output tiles (4 M tiles x 8 N tiles for the 256 x 128 case).
 #include <hip/hip_runtime.h>
