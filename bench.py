@@ -99,7 +99,8 @@ def cpu_baseline(xbits, wbits, rows):
                        f"per-128-K-block GEMM with its error bound for {rows} rows; "
                        f"{dt:.2f} s wall; quantizer single-threaded numpy, GEMM on "
                        f"{blas_threads} BLAS threads"),
-            "seconds": round(dt, 3)}
+            "seconds": round(dt, 3),
+            "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
 def device_info(torch):
@@ -117,11 +118,15 @@ def device_info(torch):
         for path in sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{kind}")):
             try:
                 with open(path) as f:
-                    cur = [l.split(":", 1)[-1].strip(" *\n") for l in f if l.rstrip().endswith("*")]
+                    lines = [l.strip() for l in f if l.strip()]
             except OSError:
                 continue
+            cur = [l.split(":", 1)[-1].strip(" *") for l in lines if l.endswith("*")]
+            if lines:
+                info[f"{kind}_max"] = lines[-1].split(":", 1)[-1].strip(" *")
             if cur:
                 info[f"{kind}_at_exit"] = cur[0]
+            if lines:
                 break
     return info
 
