@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 M, N, K = 4096, 2048, 7168
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
-PEAK_F16_TFLOPS = 2500.0        # MI355X dense f16/bf16 MFMA (the FP32-accumulating path)
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 (= f16) MFMA (the FP32-accumulating path)
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
 
@@ -38,8 +38,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "bf2bb704b82b4f124c35481356a083c6252597abd4fcd9bbf3d206674b32dd83",
-           "bytes_per_launch": 137150403,   # 120.36 MB read (FETCH_SIZE x 1.99945) + 16.79 MB written
+TRAFFIC = {"gemm_sha256": "787acd18f855ee2543439319bdea26d13ef1b587c6538e01ceb817fb12c0bb84",
+           "bytes_per_launch": 137154908,   # 120.36 MB read (FETCH_SIZE x 1.99943) + 16.79 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
@@ -329,7 +329,7 @@ def main():
     min_ms = per.min(axis=0)
     qx_bytes, qw_bytes, flops = algorithmic()
     gemm_tflops = flops / (avg_ms[2] * 1e-3) / 1e12
-    peak = PEAK_F16_TFLOPS if args.accum == "fp32" else PEAK_FP8_TFLOPS
+    peak = PEAK_BF16_TFLOPS if args.accum == "fp32" else PEAK_FP8_TFLOPS
 
     # For context: the other accumulation mode's GEMM on the same codes.
     other = 1 - accum
@@ -480,7 +480,7 @@ def main():
                                 "GB/s": round(qw_gbps, 1), "frac_hbm": round(qw_gbps / PEAK_HBM_GBPS, 4),
                                 "bytes": qw_bytes, "back_to_back_us": round(qw_b2b_us, 2),
                                 "back_to_back_frac_hbm": round(qw_bytes / qw_b2b_us / 1e3 / PEAK_HBM_GBPS, 4)},
-            "blockscaled_gemm": {"accum": args.accum, "mfma": "f16" if args.accum == "fp32" else "fp8",
+            "blockscaled_gemm": {"accum": args.accum, "mfma": "bf16" if args.accum == "fp32" else "fp8",
                                  "avg_us": round(avg_ms[2] * 1e3, 2), "median_us": round(med_ms[2] * 1e3, 2),
                                  "min_us": round(min_ms[2] * 1e3, 2),
                                  "TFLOP/s": round(gemm_tflops, 2),

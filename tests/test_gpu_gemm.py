@@ -330,7 +330,7 @@ def test_gemm_zero_m_is_noop():
 # ---------------------------------------------------------------- FP8-MFMA accumulation
 def test_accumulation_exact_vs_fp8_group_truncation():
     """One large and seven small products in one group of 8 consecutive K:
-    256*256 + 7*(2*2) = 65564 is exact in fp32.  The default path (f16 matrix
+    256*256 + 7*(2*2) = 65564 is exact in fp32.  The default path (bf16 matrix
     instructions) must return it; the FP8 matrix instructions keep only bits
     down to 2^-13 of the group's largest product and return 65536, which is
     why the default path does not use them."""
