@@ -234,16 +234,16 @@ __global__ __launch_bounds__(256) void quant_128x1_t_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
-// 128x128 blocks.  One workgroup of kThreads threads per block: thread t
-// holds columns 8*(t%16)..+8 of rows t/16 + (kThreads/16) p, i.e.
-// 2048/kThreads rows of 8 values in registers.  Block amax: per-thread max,
+// 128x128 blocks.  One workgroup of kThreads (default 256) threads per
+// block: thread t holds columns 8*(t%16)..+8 of rows t/16 + (kThreads/16) p,
+// i.e. 2048/kThreads rows of 8 values in registers.  Block amax: per-thread max,
 // wave max, then the waves through LDS.  With the transposed copy requested,
 // the codes go through LDS (row pitch 132 bytes) and each of the first 256
 // threads transposes one 8x8 byte sub-block with byte permutes, writing
 // 8-byte pieces of the transposed rows.
 constexpr int kCPitch = 132;  // bytes
 #ifndef FP8BS_W_THREADS
-#define FP8BS_W_THREADS 512
+#define FP8BS_W_THREADS 256
 #endif
 #ifndef FP8BS_W_GRID
 #define FP8BS_W_GRID 65536
