@@ -103,6 +103,69 @@ def cpu_baseline(xbits, wbits, rows):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
+def extra_cpu_baselines():
+    """The oracle, as it stands, on bounded samples of the other workloads.
+
+    Each sample is drawn with its workload's recipe (same distributions and
+    K; fewer rows), quantized by the oracle and multiplied by its float64
+    per-128-K-block reference, so every figure includes quantization.
+    Throughput is 2 * rows * cols * K of the sample over its wall time."""
+    import numpy as np
+    import oracle
+    from fp8_block_scaled_05_amd import synth
+    f32 = synth.bf16_bits_to_f32
+    res = {}
+
+    def timed(name, flops, sample, fn):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        res[name] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+                     "sample": sample, "seconds": round(dt, 3)}
+
+    k = 7168
+    # Dense FFN: 1024 rows of X, 2048 rows (16 row blocks) of the block-spread W.
+    x = f32(synth.normal_bf16(synth.rng_for(3, synth.X_ID), (1024, k), 1.0, 0.001, 100.0))
+    w = f32(synth.block_spread_bf16(synth.rng_for(3, synth.W_ID), (2048, k), 0.02))
+
+    def ffn():
+        a, sa = oracle.quant_1x128(x)
+        b, sb = oracle.quant_128x128(w)
+        oracle.blockscaled_gemm_ref(a, sa, b, sb)
+    timed("ffn_8192x18432x7168", 2.0 * 1024 * 2048 * k,
+          "X[1024,7168] 1x128 + W[2048,7168] 128x128 (block spread) + GEMM 1024x2048x7168", ffn)
+
+    # MoE: one expert's full weight [4096, 7168] and 512 of its tokens.
+    x = f32(synth.normal_bf16(synth.rng_for(4, synth.X_ID), (512, k), 1.0, 0.001, 100.0))
+    w = f32(synth.weight(4, 4096, k, expert=0))
+
+    def moe():
+        a, sa = oracle.quant_1x128(x)
+        b, sb = oracle.quant_128x128(w)
+        oracle.grouped_gemm_ref(np.array([0, 512], np.int32), a, sa, b[None], sb[None])
+    timed("moe_grouped_32768x4096x7168_g16", 2.0 * 512 * 4096 * k,
+          "one expert: X[512,7168] 1x128 + W[4096,7168] 128x128 + grouped GEMM 512x4096x7168", moe)
+
+    # Backward: 1024 tokens.  dgrad dY[1024,2048] x W[2048,7168] (W quantized
+    # 128x128, used transposed); wgrad X^T dY with both operands 128x1 along
+    # the tokens.
+    t, h, f = 1024, 7168, 2048
+    dy = f32(synth.normal_bf16(synth.rng_for(5, synth.DY_ID), (t, f), 1e-3))
+    x = f32(synth.normal_bf16(synth.rng_for(5, synth.X_ID), (t, h), 1.0, 0.001, 100.0))
+    w = f32(synth.weight(5, f, h))
+
+    def backward():
+        g, sg = oracle.quant_1x128(dy)
+        b, sb = oracle.quant_128x128(w)
+        oracle.blockscaled_gemm_ref(g, sg, np.ascontiguousarray(b.T), np.ascontiguousarray(sb.T))
+        xt, sxt = oracle.quant_128x1_t(x)
+        gt, sgt = oracle.quant_128x1_t(dy)
+        oracle.blockscaled_gemm_ref(xt, sxt, gt, sgt, "row")
+    timed("backward_dgrad_wgrad", 2.0 * (t * h * f) * 2,
+          "1024 tokens: dY 1x128 + W 128x128 + dgrad 1024x7168x2048; X and dY 128x1 + wgrad 7168x2048x1024", backward)
+    return res
+
+
 def device_info(torch):
     """Name, compute units and current clock levels of cuda:0.
 
@@ -523,6 +586,9 @@ def main():
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xbits, wbits, args.cpu_rows)
+        if args.extra_workloads:
+            print("[bench] timing the CPU oracle on samples of the other workloads", file=sys.stderr, flush=True)
+            result["extra_workloads"]["cpu_baseline"] = extra_cpu_baselines()
     print(json.dumps(result), flush=True)
     return 0
 
