@@ -571,6 +571,30 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     }
 #undef FP8BS_STEP2
   } else {
+  if constexpr (kGrouped) {
+    // A wave whose TM-row slab lies entirely past its group's last row (in
+    // an expert's tail tile) has nothing to multiply.  It issues its share
+    // of the stage and scale loads and takes the same barriers, with the
+    // same waits, as the main loop below, then leaves: no barrier follows
+    // the last one here, and its rows are not stored.
+    if (int64_t(wm) * C::TM >= rows) {
+      load_scales(0);
+      load_stage(st0, 0);
+      if (KB > 1) {
+        load_stage(st1, 1);
+        wait_and_barrier<kLoadsPerStage>();
+      } else {
+        wait_and_barrier<0>();
+      }
+      for (int kb = 0; kb < KB; ++kb) {
+        if ((kb & 3) == 1 && kb + 3 < KB) load_scales((kb >> 2) + 1);
+        if (kb + 2 < KB) load_stage(kb % 3 == 0 ? st2 : (kb % 3 == 1 ? st0 : st1), kb + 2);
+        if (kb + 2 < KB) wait_and_barrier<kLoadsPerStage>();
+        else if (kb + 1 < KB) wait_and_barrier<0>();
+      }
+      return;
+    }
+  }
   // Prologue: scales of K blocks 0..3 and K blocks 0 and 1 in flight,
   // block 0 visible, its slice 0 read.
   load_scales(0);
