@@ -276,8 +276,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   const int KB = args.KB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave % C::WM;
-  const int wn = wave / C::WM;
+  // Wave w runs on SIMD w % 4.  Consecutive waves take the WN column slabs
+  // of one row slab, so a row slab is spread over WN SIMDs (an expert's
+  // tail tile with few rows then keeps several SIMDs busy).
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
   const int r32 = lane & 31;
   const int hk = lane >> 5;
 
