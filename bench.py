@@ -38,8 +38,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "947ff2f1d0c70f5ef88c9d475b48ff968fb1625ebe9450808fcee5aded2750df",
-           "bytes_per_launch": 137158696,   # 120.37 MB read (FETCH_SIZE x 1.99948) + 16.79 MB written
+TRAFFIC = {"gemm_sha256": "3f6cf08b0c5a964d01f11c467d2f8c9eefbd5444f25db659adcecae7418dfd3f",
+           "bytes_per_launch": 137155718,   # 120.38 MB read (FETCH_SIZE x 1.99948) + 16.78 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 # The quantizers' figures come from 50 back-to-back launches on the rotating
