@@ -110,13 +110,14 @@ def cpu_baseline(xbits, wbits, rows):
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
-def extra_cpu_baselines():
+def extra_cpu_baselines(shrink=1):
     """The oracle, as it stands, on bounded samples of the other workloads.
 
     Each sample is drawn with its workload's recipe (same distributions and
     K; fewer rows), quantized by the oracle and multiplied by its float64
     per-128-K-block reference, so every figure includes quantization.
-    Throughput is 2 * rows * cols * K of the sample over its wall time."""
+    Throughput is 2 * rows * cols * K of the sample over its wall time.
+    `shrink` divides every row count (the tests use a small sample)."""
     import numpy as np
     import oracle
     from fp8_block_scaled_05_amd import synth
@@ -131,32 +132,33 @@ def extra_cpu_baselines():
                      "sample": sample, "seconds": round(dt, 3)}
 
     k = 7168
+    r1, r2, r4 = 1024 // shrink, 2048 // shrink, 4096 // shrink
     # Dense FFN: 1024 rows of X, 2048 rows (16 row blocks) of the block-spread W.
-    x = f32(synth.normal_bf16(synth.rng_for(3, synth.X_ID), (1024, k), 1.0, 0.001, 100.0))
-    w = f32(synth.block_spread_bf16(synth.rng_for(3, synth.W_ID), (2048, k), 0.02))
+    x = f32(synth.normal_bf16(synth.rng_for(3, synth.X_ID), (r1, k), 1.0, 0.001, 100.0))
+    w = f32(synth.block_spread_bf16(synth.rng_for(3, synth.W_ID), (r2, k), 0.02))
 
     def ffn():
         a, sa = oracle.quant_1x128(x)
         b, sb = oracle.quant_128x128(w)
         oracle.blockscaled_gemm_ref(a, sa, b, sb)
-    timed("ffn_8192x18432x7168", 2.0 * 1024 * 2048 * k,
-          "X[1024,7168] 1x128 + W[2048,7168] 128x128 (block spread) + GEMM 1024x2048x7168", ffn)
+    timed("ffn_8192x18432x7168", 2.0 * r1 * r2 * k,
+          f"X[{r1},7168] 1x128 + W[{r2},7168] 128x128 (block spread) + GEMM {r1}x{r2}x7168", ffn)
 
     # MoE: one expert's full weight [4096, 7168] and 512 of its tokens.
-    x = f32(synth.normal_bf16(synth.rng_for(4, synth.X_ID), (512, k), 1.0, 0.001, 100.0))
-    w = f32(synth.weight(4, 4096, k, expert=0))
+    x = f32(synth.normal_bf16(synth.rng_for(4, synth.X_ID), (r1 // 2, k), 1.0, 0.001, 100.0))
+    w = f32(synth.weight(4, r4, k, expert=0))
 
     def moe():
         a, sa = oracle.quant_1x128(x)
         b, sb = oracle.quant_128x128(w)
-        oracle.grouped_gemm_ref(np.array([0, 512], np.int32), a, sa, b[None], sb[None])
-    timed("moe_grouped_32768x4096x7168_g16", 2.0 * 512 * 4096 * k,
-          "one expert: X[512,7168] 1x128 + W[4096,7168] 128x128 + grouped GEMM 512x4096x7168", moe)
+        oracle.grouped_gemm_ref(np.array([0, r1 // 2], np.int32), a, sa, b[None], sb[None])
+    timed("moe_grouped_32768x4096x7168_g16", 2.0 * (r1 // 2) * r4 * k,
+          f"one expert: X[{r1 // 2},7168] 1x128 + W[{r4},7168] 128x128 + grouped GEMM {r1 // 2}x{r4}x7168", moe)
 
     # Backward: 1024 tokens.  dgrad dY[1024,2048] x W[2048,7168] (W quantized
     # 128x128, used transposed); wgrad X^T dY with both operands 128x1 along
     # the tokens.
-    t, h, f = 1024, 7168, 2048
+    t, h, f = r1, 7168, 2048
     dy = f32(synth.normal_bf16(synth.rng_for(5, synth.DY_ID), (t, f), 1e-3))
     x = f32(synth.normal_bf16(synth.rng_for(5, synth.X_ID), (t, h), 1.0, 0.001, 100.0))
     w = f32(synth.weight(5, f, h))
@@ -169,7 +171,7 @@ def extra_cpu_baselines():
         gt, sgt = oracle.quant_128x1_t(dy)
         oracle.blockscaled_gemm_ref(xt, sxt, gt, sgt, "row")
     timed("backward_dgrad_wgrad", 2.0 * (t * h * f) * 2,
-          "1024 tokens: dY 1x128 + W 128x128 + dgrad 1024x7168x2048; X and dY 128x1 + wgrad 7168x2048x1024", backward)
+          f"{t} tokens: dY 1x128 + W 128x128 + dgrad {t}x7168x2048; X and dY 128x1 + wgrad 7168x2048x{t}", backward)
     return res
 
 

@@ -54,3 +54,15 @@ def test_traffic_record_names_its_gemm_source():
         # read once, bf16 output written once).
         operands = 4096 * 7168 + 2048 * 7168 + 4 * (4096 * 56 + 16 * 56)
         assert rec["bytes_per_launch"] >= operands + 4096 * 2048 * 2
+
+
+def test_extra_oracle_samples_run():
+    # The oracle leg of --extra-workloads on a reduced sample: every entry
+    # names its sample and reports a positive throughput.
+    b = _bench()
+    res = b.extra_cpu_baselines(shrink=8)
+    assert set(res) == {"ffn_8192x18432x7168", "moe_grouped_32768x4096x7168_g16", "backward_dgrad_wgrad"}
+    for v in res.values():
+        assert v["kind"] == "oracle" and v["unit"] == "TFLOP/s"
+        assert v["value"] > 0 and v["seconds"] > 0 and v["sample"]
+    assert "X[128,7168]" in res["ffn_8192x18432x7168"]["sample"]
