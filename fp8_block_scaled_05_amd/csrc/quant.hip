@@ -84,10 +84,14 @@ constexpr int kActU = FP8BS_ACT_U;
 // Code stores cover whole cache lines per wave and are not read again here,
 // so they stream past the caches (nontemporal).  Scale stores are 16 bytes
 // per wave and step; they stay ordinary stores so that L2 merges them into
-// whole lines before they reach memory.
+// whole lines before they reach memory.  The weight quantizer stores its
+// codes as ordinary stores when they fit well inside the 256 MB Infinity
+// Cache (kNT false): the GEMM that follows then finds them there, and the
+// kernel itself ran faster that way at those sizes.
+template <bool kNT = true>
 __device__ __forceinline__ void store_codes8(uint8_t* dst, uint2 c) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  if (FP8BS_NT_STORE) __builtin_nontemporal_store(u32x2{c.x, c.y}, reinterpret_cast<u32x2*>(dst));
+  if (kNT && FP8BS_NT_STORE) __builtin_nontemporal_store(u32x2{c.x, c.y}, reinterpret_cast<u32x2*>(dst));
   else *reinterpret_cast<uint2*>(dst) = c;
 }
 __device__ __forceinline__ void store_scale(float* dst, float s) { *dst = s; }
@@ -245,6 +249,9 @@ constexpr int kCPitch = 132;  // bytes
 #ifndef FP8BS_W_THREADS
 #define FP8BS_W_THREADS 256
 #endif
+#ifndef FP8BS_W_CACHED_BYTES
+#define FP8BS_W_CACHED_BYTES (192ll << 20)
+#endif
 #ifndef FP8BS_W_GRID
 #define FP8BS_W_GRID 65536
 #endif
@@ -311,7 +318,7 @@ __device__ __forceinline__ void unpack8(const u32x4 (&d)[kBf16 ? 1 : 2], float (
 // b / col_blocks, column block b % col_blocks), reading block i + 1 into
 // registers while block i is reduced, encoded and stored, so that loads and
 // stores of different blocks overlap.
-template <bool kBf16, bool kTrans, int kThreads>
+template <bool kBf16, bool kTrans, int kThreads, bool kNT>
 __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __restrict__ w, int64_t ld_w,
                                                                  int64_t rows, int64_t cols,
                                                                  uint8_t* __restrict__ q, int64_t ld_q,
@@ -361,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
     for (int p = 0; p < kRows; ++p) {
       const uint2 codes = encode8<kBf16>(v[p], s, r);
       const int rr = rbase + kRowStep * p;
-      store_codes8(q + (r0 + rr) * ld_q + c0 + cc, codes);
+      store_codes8<kNT>(q + (r0 + rr) * ld_q + c0 + cc, codes);
       if constexpr (kTrans) {
         ct[(rr * kCPitch + cc) / 4] = codes.x;
         ct[(rr * kCPitch + cc) / 4 + 1] = codes.y;
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
         transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], col_hi[4], col_hi[5], col_hi[6], col_hi[7]);
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj)
-          store_codes8(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
+          store_codes8<kNT>(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
       }
       __syncthreads();   // ct is rewritten by the next block
     }
@@ -648,14 +655,18 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
   const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
   const bool bf16 = w_dtype == FP8BS_BF16;
   constexpr int kT = FP8BS_W_THREADS;
-  if (bf16 && q_t)
-    hipLaunchKernelGGL((quant_128x128_kernel<true, true, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
-  else if (bf16)
-    hipLaunchKernelGGL((quant_128x128_kernel<true, false, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
-  else if (q_t)
-    hipLaunchKernelGGL((quant_128x128_kernel<false, true, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
-  else
-    hipLaunchKernelGGL((quant_128x128_kernel<false, false, kT>), grid, dim3(kT), 0, stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  // Codes (and their transposed copy) up to FP8BS_W_CACHED_BYTES are written
+  // with ordinary stores, larger outputs stream past the caches.
+  const bool cached = rows * cols * (q_t ? 2 : 1) <= int64_t(FP8BS_W_CACHED_BYTES);
+#define FP8BS_WL(B, T, NT) hipLaunchKernelGGL((quant_128x128_kernel<B, T, kT, NT>), grid, dim3(kT), 0, stream, \
+                                              w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
+#define FP8BS_WL2(B, T) if (cached) FP8BS_WL(B, T, false); else FP8BS_WL(B, T, true);
+  if (bf16 && q_t) { FP8BS_WL2(true, true) }
+  else if (bf16) { FP8BS_WL2(true, false) }
+  else if (q_t) { FP8BS_WL2(false, true) }
+  else { FP8BS_WL2(false, false) }
+#undef FP8BS_WL2
+#undef FP8BS_WL
   return check_launch(fn);
 }
 
