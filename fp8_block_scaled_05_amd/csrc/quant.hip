@@ -84,10 +84,11 @@ constexpr int kActU = FP8BS_ACT_U;
 // Code stores cover whole cache lines per wave and are not read again here,
 // so they stream past the caches (nontemporal).  Scale stores are 16 bytes
 // per wave and step; they stay ordinary stores so that L2 merges them into
-// whole lines before they reach memory.  The weight quantizer stores its
-// codes as ordinary stores when they fit well inside the 256 MB Infinity
-// Cache (kNT false): the GEMM that follows then finds them there, and the
-// kernel itself ran faster that way at those sizes.
+// whole lines before they reach memory.  The 128x128 and dual-orientation
+// quantizers store their codes as ordinary stores when they fit well inside
+// the 256 MB Infinity Cache (kNT false): the GEMM that follows then finds
+// them there, and those kernels themselves ran faster that way at those
+// sizes (the 1x128 kernel did not).
 template <bool kNT = true>
 __device__ __forceinline__ void store_codes8(uint8_t* dst, uint2 c) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -249,8 +250,8 @@ constexpr int kCPitch = 132;  // bytes
 #ifndef FP8BS_W_THREADS
 #define FP8BS_W_THREADS 256
 #endif
-#ifndef FP8BS_W_CACHED_BYTES
-#define FP8BS_W_CACHED_BYTES (192ll << 20)
+#ifndef FP8BS_CACHED_CODE_BYTES
+#define FP8BS_CACHED_CODE_BYTES (192ll << 20)
 #endif
 #ifndef FP8BS_W_GRID
 #define FP8BS_W_GRID 65536
@@ -429,7 +430,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
 // one were last read before the previous one.
 // kRowOut false: only the 128x1 output (the 128x1_T tiling of
 // fp8_quant_act_1x128 when cols is a multiple of 128).
-template <bool kBf16, int kThreads, bool kRowOut>
+template <bool kBf16, int kThreads, bool kRowOut, bool kNT>
 __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __restrict__ x, int64_t ld_x,
                                                               int64_t rows, int64_t cols,
                                                               uint8_t* __restrict__ q, int64_t ld_q,
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
         const float s = tile_scale(row16_max(absmax8(v[p])));
         const float r = 1.0f / s;
         const int64_t row = r0 + rbase + kRowStep * p;
-        store_codes8(q + row * ld_q + c0 + cc, encode8<kBf16>(v[p], s, r));
+        store_codes8<kNT>(q + row * ld_q + c0 + cc, encode8<kBf16>(v[p], s, r));
         if ((t & 15) == 0) store_scale(&scale[row * row_kb + bj], s);
       }
     }
@@ -547,7 +548,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
       transpose4x4_bytes(hi[4], hi[5], hi[6], hi[7], col_hi[4], col_hi[5], col_hi[6], col_hi[7]);
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        store_codes8(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
+        store_codes8<kNT>(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
     }
     cur = nxt;
   }
@@ -608,12 +609,12 @@ extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int6
     const int64_t per_wg = (n_blocks + FP8BS_DUAL_GRID - 1) / FP8BS_DUAL_GRID;
     const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
     constexpr int kT = FP8BS_DUAL_THREADS;
-    if (bf16)
-      hipLaunchKernelGGL((quant_dual_kernel<true, kT, false>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols,
-                         nullptr, int64_t(0), nullptr, q, ld_q, scale);
-    else
-      hipLaunchKernelGGL((quant_dual_kernel<false, kT, false>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols,
-                         nullptr, int64_t(0), nullptr, q, ld_q, scale);
+    const bool cached = rows * cols <= int64_t(FP8BS_CACHED_CODE_BYTES);
+#define FP8BS_TL(B, NT) hipLaunchKernelGGL((quant_dual_kernel<B, kT, false, NT>), grid, dim3(kT), 0, stream, x, ld_x, \
+                                           rows, cols, nullptr, int64_t(0), nullptr, q, ld_q, scale)
+    if (bf16) { if (cached) FP8BS_TL(true, false); else FP8BS_TL(true, true); }
+    else { if (cached) FP8BS_TL(false, false); else FP8BS_TL(false, true); }
+#undef FP8BS_TL
   } else {
     if ((cols + 63) / 64 > 0x7fffffff || rows / 128 > 65535)
       return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles for the launch grid", fn);
@@ -655,9 +656,9 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
   const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
   const bool bf16 = w_dtype == FP8BS_BF16;
   constexpr int kT = FP8BS_W_THREADS;
-  // Codes (and their transposed copy) up to FP8BS_W_CACHED_BYTES are written
+  // Codes (and their transposed copy) up to FP8BS_CACHED_CODE_BYTES are written
   // with ordinary stores, larger outputs stream past the caches.
-  const bool cached = rows * cols * (q_t ? 2 : 1) <= int64_t(FP8BS_W_CACHED_BYTES);
+  const bool cached = rows * cols * (q_t ? 2 : 1) <= int64_t(FP8BS_CACHED_CODE_BYTES);
 #define FP8BS_WL(B, T, NT) hipLaunchKernelGGL((quant_128x128_kernel<B, T, kT, NT>), grid, dim3(kT), 0, stream, \
                                               w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
 #define FP8BS_WL2(B, T) if (cached) FP8BS_WL(B, T, false); else FP8BS_WL(B, T, true);
@@ -694,9 +695,11 @@ extern "C" fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64
   const int64_t per_wg = (n_blocks + FP8BS_DUAL_GRID - 1) / FP8BS_DUAL_GRID;
   const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
   constexpr int kT = FP8BS_DUAL_THREADS;
-  if (x_dtype == FP8BS_BF16)
-    hipLaunchKernelGGL((quant_dual_kernel<true, kT, true>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
-  else
-    hipLaunchKernelGGL((quant_dual_kernel<false, kT, true>), grid, dim3(kT), 0, stream, x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t);
+  const bool cached = 2 * rows * cols <= int64_t(FP8BS_CACHED_CODE_BYTES);
+#define FP8BS_DL(B, NT) hipLaunchKernelGGL((quant_dual_kernel<B, kT, true, NT>), grid, dim3(kT), 0, stream, x, ld_x, \
+                                           rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
+  if (x_dtype == FP8BS_BF16) { if (cached) FP8BS_DL(true, false); else FP8BS_DL(true, true); }
+  else { if (cached) FP8BS_DL(false, false); else FP8BS_DL(false, true); }
+#undef FP8BS_DL
   return check_launch(fn);
 }
