@@ -16,17 +16,20 @@ Test infrastructure only (see the package docstring).
 * Formats: E4M3 (max 448) for activations and weights; E5M2 (max 57344) for
   gradients in the hybrid recipe (``e5m2``).
 
-Precision reading: everything in float32, as for the fine-grained quantizer:
-amax, (1 + margin), the widened amax, the division by the format maximum and
-x / s are each one float32 operation.
+Precision reading.  The page computes the scale on Python floats: ``.item()``
+turns the tensor's amax into a binary64 value (exactly), and (1 + margin), the
+widened amax, the division by 448.0 and the ``scale < 1e-6`` test are binary64
+operations.  The oracle does the same and rounds the result once to float32,
+the precision in which the scale is stored and in which x / s is taken (one
+float32 division, as the fine-grained quantizer takes it).
 """
 import numpy as np
 
 from .e4m3 import e4m3_encode
 from .e5m2 import e5m2_encode
 
-FORMATS = {"e4m3": (np.float32(448.0), e4m3_encode), "e5m2": (np.float32(57344.0), e5m2_encode)}
-TENSOR_GUARD = np.float32(1e-6)
+FORMATS = {"e4m3": (448.0, e4m3_encode), "e5m2": (57344.0, e5m2_encode)}
+TENSOR_GUARD = 1e-6          # the page's "scale too small" threshold, a Python float
 
 
 def _finite(x):
@@ -37,11 +40,15 @@ def _finite(x):
 
 
 def tensor_scale(amax, fmt="e4m3", margin=0.0):
-    """s = fl32(fl32(amax * fl32(1 + margin)) / fmt_max); s := 1 if s < fl32(1e-6)."""
+    """SafeFP8Quantizer's scale: d = amax * (1 + margin) / fmt_max on Python
+    floats (binary64, the page's order of operations); 1.0 if d < 1e-6; then
+    rounded once to float32."""
     fmax, _ = FORMATS[fmt]
-    widen = np.float32(1.0) + np.float32(margin)
-    s = np.float32(np.float32(amax) * widen) / fmax
-    return np.float32(1.0) if s < TENSOR_GUARD else np.float32(s)
+    dynamic_amax = float(amax) * (1.0 + float(margin))
+    d = dynamic_amax / fmax
+    if d < TENSOR_GUARD:
+        return np.float32(1.0)
+    return np.float32(d)
 
 
 def quant_tensor_current(x, fmt="e4m3", margin=0.0):

@@ -18,12 +18,10 @@ def f32_from_bits(u):
     return struct.unpack("<f", struct.pack("<I", u))[0]
 
 
-def rn32(q):
-    """Round a rational to the nearest binary32 value, ties to even.
-
-    Returns a Python float holding the binary32 value (sign of zero aside).
-    Handles subnormals; assumes no overflow.
-    """
+def _round_binary(q, p, emin):
+    """Nearest binary floating-point value with p significand bits and
+    minimum normal exponent emin, ties to even (subnormals handled, no
+    overflow), as a Python float (sign of zero aside)."""
     q = Fraction(q)
     if q == 0:
         return 0.0
@@ -35,8 +33,8 @@ def rn32(q):
         e -= 1
     if Fraction(2) ** (e + 1) <= a:
         e += 1
-    e = max(e, -126)
-    quantum = Fraction(2) ** (e - 23)
+    e = max(e, emin)
+    quantum = Fraction(2) ** (e - (p - 1))
     n = a / quantum
     fl = n.numerator // n.denominator
     rem = n - fl
@@ -44,6 +42,20 @@ def rn32(q):
         fl += 1
     v = float(fl * quantum)
     return -v if neg else v
+
+
+def rn32(q):
+    """Round a rational to the nearest binary32 value, ties to even.
+
+    Returns a Python float holding the binary32 value (sign of zero aside).
+    Handles subnormals; assumes no overflow.
+    """
+    return _round_binary(q, 24, -126)
+
+
+def rn64(q):
+    """Round a rational to the nearest binary64 value, ties to even."""
+    return _round_binary(q, 53, -1022)
 
 
 # E4M3 magnitudes built from the bit fields, as exact integers in units of 2^-9.
@@ -151,18 +163,20 @@ def e5m2_encode_exact(v, neg_zero=False):
 
 
 def tensor_quantize_exact(values, fmt_max, encode_exact, margin=0.0, amax=None):
-    """Per-tensor scaling by exact arithmetic: each float32 step rounded once.
+    """Per-tensor scaling by exact arithmetic, each step rounded once.
 
-    s = rn32(rn32(amax * rn32(1 + margin)) / fmt_max), s := 1 if s < rn32(1e-6);
-    codes = encode(rn32(x / s)).  `amax` overrides the tensor's own (delayed).
+    The scale takes the page's Python-float (binary64) steps:
+    d = rn64(rn64(amax * rn64(1 + margin)) / fmt_max); s = 1 if d < 1e-6
+    (the binary64 literal), else s = rn32(d).  Codes: encode(rn32(x / s)).
+    `margin` is the binary64 value passed; `amax` overrides the tensor's own
+    (delayed scaling).
     """
     vals = [float(v) for v in values]
     if amax is None:
         amax = max(abs(v) for v in vals)
-    widen = rn32(1 + Fraction(f32_from_bits(f32_bits(margin))))
-    s = rn32(rn32(Fraction(amax) * Fraction(widen)) / fmt_max)
-    if s < rn32(Fraction(1e-6)):
-        s = 1.0
+    widen = rn64(1 + Fraction(float(margin)))
+    d = rn64(Fraction(rn64(Fraction(amax) * Fraction(widen))) / fmt_max)
+    s = 1.0 if Fraction(d) < Fraction(1e-6) else rn32(Fraction(d))
     codes = [encode_exact(rn32(Fraction(x) / Fraction(s)), neg_zero=math.copysign(1.0, x) < 0)
              for x in vals]
     return codes, s

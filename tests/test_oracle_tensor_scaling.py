@@ -13,9 +13,50 @@ def test_scale_closed_forms():
     assert oracle.tensor_scale(np.float32(0.0)) == np.float32(1.0)                 # guard
     assert oracle.tensor_scale(np.float32(448e-6 * 0.99)) == np.float32(1.0)       # s < 1e-6
     assert oracle.tensor_scale(np.float32(896.0), margin=0.0) == np.float32(2.0)
-    # margin 0.15: fl32(1.15) and one rounding per step
-    s = oracle.tensor_scale(np.float32(448.0), margin=0.15)
-    assert s == np.float32(np.float32(448.0) * np.float32(1.15)) / np.float32(448.0)
+    # margin 1 doubles the amax exactly: 448 * 2 / 448 = 2
+    assert oracle.tensor_scale(np.float32(448.0), margin=1.0) == np.float32(2.0)
+    # margin 0: one float32 rounding of amax / 448 (rounding the binary64
+    # quotient again to float32 cannot change it)
+    for a in (1.0, 3.0, 1e-3, 7.5e5):
+        assert oracle.tensor_scale(np.float32(a)) == exact.rn32(exact.Fraction(float(np.float32(a))) / 448)
+
+
+def test_scale_follows_binary64_steps():
+    """The scale takes the page's Python-float steps and one final float32
+    rounding.  A chain of float32 operations would differ in the last bit for
+    a good share of amax values at margins 0.1 / 0.15, so these values tell the
+    two readings apart."""
+    rng = np.random.default_rng(64)
+    amaxes = (rng.standard_normal(3000) * np.exp2(rng.uniform(-20, 20, 3000))).astype(np.float32)
+    differ = 0
+    for margin in (0.1, 0.15):
+        for a in np.abs(amaxes):
+            got = oracle.tensor_scale(a, margin=margin)
+            _, want = exact.tensor_quantize_exact([float(a)], 448, exact.e4m3_encode_exact, margin)
+            assert float(got) == want, (a, margin)
+            f32_chain = np.float32(np.float32(a * np.float32(np.float32(1) + np.float32(margin))) / np.float32(448))
+            differ += int(f32_chain != got)
+    assert differ > 0.1 * 2 * len(amaxes)
+
+
+def test_current_scaling_against_torch_cpu_cast():
+    """SafeFP8Quantizer's steps done with torch on the CPU for a float32
+    tensor: amax through .item(), the scale on Python floats, the quotient in
+    float32 and torch's E4M3 cast.  Its codes and scale equal the oracle's."""
+    import torch
+    rng = np.random.default_rng(65)
+    for margin in (0.1, 0.15, 0.0):
+        x = (rng.standard_normal((48, 40)) * np.exp2(rng.uniform(-6, 6))).astype(np.float32)
+        t = torch.from_numpy(x)
+        amax = torch.abs(t).max().item()
+        scale = amax * (1 + margin) / 448.0
+        if scale < 1e-6:
+            scale = 1.0
+        want = (t / scale).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        codes, s, a = oracle.quant_tensor_current(x, "e4m3", margin)
+        assert a == np.float32(amax)
+        assert s == np.float32(scale)
+        assert np.array_equal(codes, want)
 
 
 def test_current_scaling_matches_exact_arithmetic():
