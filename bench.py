@@ -4,18 +4,23 @@ One step = online 1x128 quantization of the activations X [4096, 7168] (bf16),
 128x128 quantization of the weight W [2048, 7168] (bf16), and the block-scaled
 FP8 GEMM Y = X W^T [4096, 2048] with FP32 promotion per 128-deep K block
 (bf16 output by default).  Inputs are seeded synthetic tensors shaped like a
-DeepSeek-V3 layer (hidden 7168), already resident in HBM; W steps through
-several copies and X/Y through several buffers so that more than 1 GiB is
-cycled and the 256 MB Infinity Cache cannot serve repeated reads.
+DeepSeek-V3 layer (hidden 7168), already resident in HBM; X, W and Y step
+through several buffer sets so that more than 1 GiB is cycled and the 256 MB
+Infinity Cache cannot serve repeated reads.
 
-Prints one JSON line.  `value` is whole-step throughput in TFLOP/s
-(2*M*N*K per step over the measured step time, quantization included); the
-`roofline` object covers the dominant kernel (the GEMM) with its average
-launch duration from HIP events recorded on the stream the kernels run on,
-around each kernel of every 8th timed step (events on every step would add
-~10 us of their own to each step's time);
-`kernels` gives the same for each kernel, the quantizers as GB/s against HBM;
-`cpu_baseline` times the CPU oracle on a bounded sample of the same step.
+Prints one JSON line:
+  value / ms_per_step  whole-step throughput: 2*M*N*K per step over the
+                       measured step time (both quantizers included);
+  roofline             the GEMM (the dominant kernel) against the 5.0 PFLOP/s
+                       dense FP8 MFMA peak, from its average launch duration
+                       over back-to-back launches on rotating buffers, timed
+                       with HIP events on the stream the kernels run on;
+  kernels              the same for every kernel of the step and the other
+                       kernels of the library (quantizers as GB/s against HBM);
+  workloads            the other workload shapes (dense FFN, MoE grouped,
+                       dgrad/wgrad) with their GEMMs and quantizers;
+  cpu_baseline         the CPU oracle timed on a bounded sample of the step
+                       (and of the other workloads), with the cores it used.
 """
 import argparse
 import ctypes
@@ -30,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 M, N, K = 4096, 2048, 7168
 PEAK_FP8_TFLOPS = 5000.0        # MI355X dense FP8 MFMA
-PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 (= f16) MFMA (the FP32-accumulating path)
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 (= f16) MFMA, on which the exact GEMM runs
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
 
@@ -42,13 +47,6 @@ TRAFFIC = {"gemm_sha256": "3f6cf08b0c5a964d01f11c467d2f8c9eefbd5444f25db659adcec
            "bytes_per_launch": 137155718,   # 120.38 MB read (FETCH_SIZE x 1.99948) + 16.78 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
-# The quantizers' figures come from 50 back-to-back launches on the rotating
-# buffers.  Their in-step durations from the sampled steps' events are also
-# reported; on kernels this short those include a few microseconds of the
-# events' own records (a kernel trace of the same steps, without events, gives
-# durations within 2% of the back-to-back ones).
-IN_STEP_NOTE = ("avg_us/GB/s/frac_hbm: 50 back-to-back launches on rotating buffers; "
-                "in_step_events: sampled steps' events, which add their own few microseconds")
 
 
 def algorithmic():
@@ -59,54 +57,76 @@ def algorithmic():
     return quant_x_bytes, quant_w_bytes, gemm_flops
 
 
+def quant_bytes(rows, cols, kind):
+    """Algorithmic bytes of one quantizer call on a bf16 [rows, cols] input:
+    input read once, each output written once."""
+    n = rows * cols
+    if kind in ("1x128", "128x1_t"):
+        return 2 * n + n + 4 * (n // 128)
+    if kind == "128x128":
+        return 2 * n + n + 4 * (n // (128 * 128))
+    if kind == "128x128+t":
+        return 2 * n + 2 * n + 4 * (n // (128 * 128))
+    if kind == "dual":
+        return 2 * n + 2 * n + 2 * 4 * (n // 128)
+    raise ValueError(kind)
+
+
 def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--launches", type=int, default=50,
+                   help="back-to-back launches per kernel figure (at least 50)")
     p.add_argument("--out", choices=["bf16", "f32"], default="bf16")
-    p.add_argument("--accum", choices=["fp32", "fp8_mfma"], default="fp32",
-                   help="block-partial accumulation of the GEMM (see include/fp8bs.h)")
-    p.add_argument("--event-every", type=int, default=8,
-                   help="record per-kernel events on every Nth timed step (1 = every step)")
     p.add_argument("--rotate-mib", type=int, default=1100,
                    help="bytes of input/output buffers cycled through (defeats the MALL)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=M,
                    help="rows of X in the oracle's timed sample (default: all)")
-    p.add_argument("--extra-workloads", action="store_true",
-                   help="also time the GEMMs (and quantizers) of the other workload shapes: dense FFN, "
-                        "MoE grouped, dgrad and wgrad (reported under extra_workloads)")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the other workload shapes (dense FFN, MoE grouped, dgrad/wgrad)")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run one device copy of 128 MiB (counter calibration for rocprofv3 --pmc)")
-    return p.parse_args()
+    a = p.parse_args()
+    a.launches = max(50, a.launches)
+    return a
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001 - threadpoolctl is optional
+        return 1
 
 
 def cpu_baseline(xbits, wbits, rows):
     """The oracle, as it stands, on the first `rows` rows of X and all of W."""
-    import numpy as np
     import oracle
     from fp8_block_scaled_05_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001 - threadpoolctl is optional
-        blas_threads = 1
+    nthreads = blas_threads()
     x = synth.bf16_bits_to_f32(xbits[:rows])
     w = synth.bf16_bits_to_f32(wbits)
     t0 = time.perf_counter()
     a, sa = oracle.quant_1x128(x)
     b, sb = oracle.quant_128x128(w)
-    y, _ = oracle.blockscaled_gemm_ref(a, sa, b, sb)
-    dt = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    oracle.blockscaled_gemm_ref(a, sa, b, sb)
+    t2 = time.perf_counter()
+    dt = t2 - t0
     flops = 2.0 * rows * N * K
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads),
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(nthreads),
             "kind": "oracle",
             "sample": (f"quantize X[:{rows}] (1x128) + W[{N},{K}] (128x128) + float64 "
                        f"per-128-K-block GEMM with its error bound for {rows} rows; "
-                       f"{dt:.2f} s wall; quantizer single-threaded numpy, GEMM on "
-                       f"{blas_threads} BLAS threads"),
+                       f"{dt:.2f} s wall"),
             "seconds": round(dt, 3),
+            "stages": {"quantize": {"seconds": round(t1 - t0, 3), "cores": 1,
+                                    "note": "single-threaded numpy"},
+                       "gemm": {"seconds": round(t2 - t1, 3), "cores": int(nthreads),
+                                "note": "float64 BLAS"}},
             "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -122,6 +142,7 @@ def extra_cpu_baselines(shrink=1):
     import oracle
     from fp8_block_scaled_05_amd import synth
     f32 = synth.bf16_bits_to_f32
+    nthreads = blas_threads()
     res = {}
 
     def timed(name, flops, sample, fn):
@@ -129,7 +150,8 @@ def extra_cpu_baselines(shrink=1):
         fn()
         dt = time.perf_counter() - t0
         res[name] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
-                     "sample": sample, "seconds": round(dt, 3)}
+                     "sample": sample, "seconds": round(dt, 3),
+                     "cores": {"quantize": 1, "gemm": int(nthreads)}}
 
     k = 7168
     r1, r2, r4 = 1024 // shrink, 2048 // shrink, 4096 // shrink
@@ -203,87 +225,298 @@ def device_info(torch):
     return info
 
 
-def extra_workloads(L, fb, torch, dev, hs, accum):
-    """Time each other workload's kernels on operands of its exact shapes.
+class Bench:
+    """Library calls with prepared arguments and event timing on one stream."""
 
-    Codes are uniform random E4M3 bytes without NaN, scales uniform in
-    [0.5, 1.5), generated on the GPU (the values do not change the work);
-    the MoE expert counts are the workload's seeded counts.  Each kernel is
-    timed over back-to-back launches with events on the launch stream."""
-    from fp8_block_scaled_05_amd import synth
-    vp = ctypes.c_void_p
+    def __init__(self, torch, fb, launches, rotate_bytes):
+        self.torch, self.fb, self.L = torch, fb, fb.lib()
+        self.stream = torch.cuda.current_stream()
+        self.hs = ctypes.c_void_p(self.stream.cuda_stream)
+        self.launches = launches
+        self.rotate_bytes = rotate_bytes
+        self.dev = torch.device("cuda:0")
 
-    def codes(*shape):
-        return torch.randint(0, 0x7E, shape, dtype=torch.uint8, device=dev)
+    def check(self, status):
+        if status:
+            raise RuntimeError(self.fb.last_error())
 
-    def scales(*shape):
-        return torch.rand(shape, device=dev) + 0.5
+    def n_sets(self, set_bytes, cap=32):
+        """Buffer sets whose total exceeds the rotation size (at least 1)."""
+        return max(1, min(cap, -(-self.rotate_bytes // max(1, set_bytes))))
 
-    def timed(fn, n):
-        fn()
-        torch.cuda.synchronize()
+    def timed_us(self, fn, n=None, warm=3):
+        """Average microseconds per call over n back-to-back calls fn(i), with
+        events recorded on the launch stream."""
+        torch = self.torch
+        n = n or self.launches
+        for i in range(warm):
+            fn(i)
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(torch.cuda.current_stream())
-        for _ in range(n):
-            fn()
-        t1.record(torch.cuda.current_stream())
+        t0.record(self.stream)
+        for i in range(n):
+            fn(i)
+        t1.record(self.stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1) / n * 1e3
 
-    def check(st):
-        if st:
-            raise RuntimeError(fb.last_error())
+    # -- library calls on tensors (pointers only; shapes are the caller's) --
+    def quant_act(self, x, q, s, tiling=0):
+        rows, cols = x.shape
+        ldq = cols if tiling == 0 else rows
+        self.check(self.L.fp8_quant_act_1x128(x.data_ptr(), 0 if x.dtype == self.torch.bfloat16 else 1,
+                                              rows, cols, cols, tiling, q.data_ptr(), ldq, s.data_ptr(),
+                                              self.hs))
 
+    def quant_w(self, w, q, s, qt=None):
+        rows, cols = w.shape
+        self.check(self.L.fp8_quant_w_128x128(w.data_ptr(), 0, rows, cols, cols, q.data_ptr(), cols,
+                                              s.data_ptr(), qt.data_ptr() if qt is not None else None,
+                                              rows if qt is not None else 0, self.hs))
+
+    def quant_dual(self, x, q, s, qt, st):
+        rows, cols = x.shape
+        self.check(self.L.fp8_quant_act_dual(x.data_ptr(), 0, rows, cols, cols, q.data_ptr(), cols,
+                                             s.data_ptr(), qt.data_ptr(), rows, st.data_ptr(), self.hs))
+
+    def gemm(self, a, sa, b, sb, y, kind=0, entry="fp8_blockscaled_gemm"):
+        m, k = a.shape
+        n = b.shape[0]
+        ydt = 0 if y.dtype == self.torch.bfloat16 else 1
+        self.check(getattr(self.L, entry)(m, n, k, a.data_ptr(), k, sa.data_ptr(), b.data_ptr(), k,
+                                          sb.data_ptr(), kind, y.data_ptr(), ydt, n, self.hs))
+
+    def grouped(self, off, a, sa, b, sb, y):
+        m, k = a.shape
+        g, n, _ = b.shape
+        self.check(self.L.fp8_blockscaled_grouped_gemm(m, n, k, g, off.data_ptr(), a.data_ptr(),
+                                                       sa.data_ptr(), b.data_ptr(), sb.data_ptr(),
+                                                       y.data_ptr(), 0, self.hs))
+
+    # -- result records --
+    @staticmethod
+    def gemm_rec(flops, us, **extra):
+        tf = flops / us / 1e6
+        return {**extra, "avg_us": round(us, 2), "TFLOP/s": round(tf, 2),
+                "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops": int(flops)}
+
+    @staticmethod
+    def quant_rec(nbytes, us, **extra):
+        gbs = nbytes / us / 1e3
+        return {**extra, "avg_us": round(us, 2), "GB/s": round(gbs, 1),
+                "frac_hbm": round(gbs / PEAK_HBM_GBPS, 4), "bytes": int(nbytes)}
+
+
+def rand_bf16(torch, dev, shape, std=1.0, seed=0):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return (torch.randn(shape, device=dev, generator=g) * std).to(torch.bfloat16)
+
+
+def linear_kernels(B, xs, ws, ys_dtype, qx_bytes, qw_bytes, flops):
+    """Back-to-back figures of the step's kernels and the library's other
+    kernels on the linear workload's shapes."""
+    torch, dev, n = B.torch, B.dev, B.launches
+    ns = len(xs)
+    a = [torch.empty((M, K), dtype=torch.uint8, device=dev) for _ in range(ns)]
+    sa = [torch.empty((M, K // 128), dtype=torch.float32, device=dev) for _ in range(ns)]
+    b = [torch.empty((N, K), dtype=torch.uint8, device=dev) for _ in range(ns)]
+    sb = [torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev) for _ in range(ns)]
+    ys = [torch.empty((M, N), dtype=ys_dtype, device=dev) for _ in range(ns)]
+    for j in range(ns):
+        B.quant_act(xs[j], a[j], sa[j])
+        B.quant_w(ws[j], b[j], sb[j])
+    torch.cuda.synchronize()
     out = {}
+    qx_us = B.timed_us(lambda i: B.quant_act(xs[i % ns], a[i % ns], sa[i % ns]))
+    qw_us = B.timed_us(lambda i: B.quant_w(ws[i % ns], b[i % ns], sb[i % ns]))
+    both_us = B.timed_us(lambda i: (B.quant_act(xs[i % ns], a[i % ns], sa[i % ns]),
+                                    B.quant_w(ws[i % ns], b[i % ns], sb[i % ns])))
+    gemm_us = B.timed_us(lambda i: B.gemm(a[i % ns], sa[i % ns], b[i % ns], sb[i % ns], ys[i % ns]))
+    out["quant_act_1x128"] = B.quant_rec(qx_bytes, qx_us, shape=[M, K], launches=n)
+    out["quant_w_128x128"] = B.quant_rec(qw_bytes, qw_us, shape=[N, K], launches=n)
+    out["quantize_step"] = B.quant_rec(qx_bytes + qw_bytes, both_us, launches=n,
+                                       note="the step's two quantizer launches back to back (X 1x128 + W 128x128)")
+    out["blockscaled_gemm"] = B.gemm_rec(flops, gemm_us, M=M, N=N, K=K, out="bf16" if ys_dtype == torch.bfloat16 else "f32",
+                                         mfma="bf16 (E4M3 widened exactly)", launches=n)
+    fp8_us = B.timed_us(lambda i: B.gemm(a[i % ns], sa[i % ns], b[i % ns], sb[i % ns], ys[i % ns],
+                                         entry="fp8_blockscaled_gemm_fp8mma"))
+    out["blockscaled_gemm_fp8mma"] = B.gemm_rec(flops, fp8_us, mfma="fp8", launches=n,
+                                                note="FP8 matrix instructions; outside the accuracy contract")
 
-    def dense(name, m, n, k, kind, ydt, iters):
-        a, sa, b = codes(m, k), scales(m, k // 128), codes(n, k)
-        sb = scales(n // 128, k // 128) if kind == 0 else scales(n, k // 128)
-        y = torch.empty((m, n), dtype=torch.bfloat16 if ydt == 0 else torch.float32, device=dev)
-        us = timed(lambda: check(L.fp8_blockscaled_gemm(m, n, k, vp(a.data_ptr()), k, vp(sa.data_ptr()),
-                                                        vp(b.data_ptr()), k, vp(sb.data_ptr()), kind,
-                                                        vp(y.data_ptr()), ydt, n, accum, hs)), iters)
-        out[name] = {"M": m, "N": n, "K": k, "b_scales": "block128" if kind == 0 else "row",
-                     "out": "bf16" if ydt == 0 else "f32", "avg_us": round(us, 2),
-                     "TFLOP/s": round(2 * m * n * k / us / 1e6, 2)}
+    # The GEMM with its output quantized 1x128 in the epilogue, against the
+    # same result in two launches (float32 GEMM output, then the quantizer).
+    yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    ysc = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
 
-    dense("ffn_8192x18432x7168", 8192, 18432, 7168, 0, 0, 10)
-    dense("dgrad_8192x7168x2048", 8192, 7168, 2048, 0, 0, 20)
-    dense("wgrad_7168x2048x8192", 7168, 2048, 8192, 1, 1, 20)
+    def gemm_quant(i):
+        j = i % ns
+        B.check(B.L.fp8_blockscaled_gemm_quant(M, N, K, a[j].data_ptr(), K, sa[j].data_ptr(), b[j].data_ptr(), K,
+                                               sb[j].data_ptr(), 0, yq.data_ptr(), N, ysc.data_ptr(), B.hs))
 
+    def gemm_then_quant(i):
+        j = i % ns
+        B.gemm(a[j], sa[j], b[j], sb[j], y32)
+        B.quant_act(y32, yq, ysc)
+    gq_us, g2_us = B.timed_us(gemm_quant), B.timed_us(gemm_then_quant)
+    out["blockscaled_gemm_quant_out"] = B.gemm_rec(flops, gq_us, two_launch_us=round(g2_us, 2), launches=n,
+                                                   note="Y quantized 1x128 (E4M3 + scales) in the GEMM epilogue "
+                                                        "vs float32 GEMM then the quantizer")
+    del y32
+
+    # Both activation tilings from one read (dual) and the 128x1 tiling alone.
+    qd = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sd = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    qtd = torch.empty((K, M), dtype=torch.uint8, device=dev)
+    std = torch.empty((K, M // 128), dtype=torch.float32, device=dev)
+    dual_us = B.timed_us(lambda i: B.quant_dual(xs[i % ns], qd, sd, qtd, std))
+    t_us = B.timed_us(lambda i: B.quant_act(xs[i % ns], qtd, std, tiling=1))
+    out["quant_act_dual"] = B.quant_rec(quant_bytes(M, K, "dual"), dual_us, launches=n,
+                                        note="X 1x128 and 128x1 (transposed) from one read")
+    out["quant_act_128x1_t"] = B.quant_rec(quant_bytes(M, K, "128x1_t"), t_us, launches=n)
+
+    # Dequantize 1x128 codes to bf16.
+    n_deq = 4                       # 4 x (29 MB codes + 59 MB bf16 out) cycled: above the MALL
+    deq_out = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(n_deq)]
+
+    def dequant(i):
+        B.check(B.L.fp8_dequant(a[i % ns].data_ptr(), M, K, K, sa[i % ns].data_ptr(), 0,
+                                deq_out[i % n_deq].data_ptr(), 0, K, B.hs))
+    deq_us = B.timed_us(dequant)
+    out["dequant_1x128_bf16"] = B.quant_rec(M * K * 3 + 4 * M * (K // 128), deq_us, launches=n)
+    del deq_out
+
+    # Prior-art per-tensor scalings on the same X: current (two passes) and
+    # delayed (one pass, 1024-entry amax history).
+    t_scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    t_amax = torch.empty((1,), dtype=torch.float32, device=dev)
+    t_hist = torch.ones((1024,), dtype=torch.float32, device=dev)
+
+    def tensor_q(i, hist):
+        B.check(B.L.fp8_quant_tensor(xs[i % ns].data_ptr(), 0, M, K, K, 0, ctypes.c_double(0.0),
+                                     hist.data_ptr() if hist is not None else None, 1024 if hist is not None else 0,
+                                     qd.data_ptr(), K, t_scale.data_ptr(), t_amax.data_ptr(), B.hs))
+    tc_us = B.timed_us(lambda i: tensor_q(i, None))
+    td_us = B.timed_us(lambda i: tensor_q(i, t_hist))
+    out["quant_tensor_current"] = B.quant_rec(M * K * 5, tc_us, launches=n,
+                                              note="per-tensor scale (prior art): amax pass + code pass")
+    out["quant_tensor_delayed"] = B.quant_rec(M * K * 3, td_us, launches=n,
+                                              note="per-tensor scale from a 1024-entry amax history")
+    return out
+
+
+def other_workloads(B):
+    """The dense FFN, MoE grouped and backward workloads' GEMMs and
+    quantizers, each on its exact shapes.  Operands are codes and scales of
+    Gaussian bf16 tensors quantized by the library (X ~ N(0,1),
+    W ~ N(0,0.02), dY ~ N(0,1e-6)); the MoE expert counts are the
+    workload's seeded counts.  Buffer sets rotate past the Infinity Cache."""
+    from fp8_block_scaled_05_amd import synth
+    torch, dev = B.torch, B.dev
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    n_gemm = max(20, B.launches // 2)
+    res = {}
+
+    def quantize_pair(x, w, w_t=False):
+        a = torch.empty(x.shape, dtype=u8, device=dev)
+        sa = torch.empty((x.shape[0], x.shape[1] // 128), dtype=f32, device=dev)
+        B.quant_act(x, a, sa)
+        b = torch.empty(w.shape, dtype=u8, device=dev)
+        sb = torch.empty((w.shape[0] // 128, w.shape[1] // 128), dtype=f32, device=dev)
+        bt = torch.empty((w.shape[1], w.shape[0]), dtype=u8, device=dev) if w_t else None
+        B.quant_w(w, b, sb, bt)
+        return a, sa, b, sb, bt
+
+    def rotate(tensors):
+        """Copies of a set of tensors so that all sets together exceed the rotation size."""
+        nb = sum(t.numel() * t.element_size() for t in tensors)
+        ns = B.n_sets(nb, cap=8)
+        return [tensors] + [[t.clone() for t in tensors] for _ in range(ns - 1)]
+
+    # ---- dense FFN: X [8192, 7168] x W [18432, 7168]^T -> Y bf16 [8192, 18432]
+    m, n, k = 8192, 18432, 7168
+    x = rand_bf16(torch, dev, (m, k), 1.0, 31)
+    w = rand_bf16(torch, dev, (n, k), 0.02, 32)
+    a, sa, b, sb, _ = quantize_pair(x, w)
+    y = torch.empty((m, n), dtype=bf, device=dev)
+    sets = rotate([a, sa, b, sb, y])
+    us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)]), n=n_gemm)
+    qa = [torch.empty((m, k), dtype=u8, device=dev), torch.empty((m, k // 128), dtype=f32, device=dev)]
+    qb = [torch.empty((n, k), dtype=u8, device=dev), torch.empty((n // 128, k // 128), dtype=f32, device=dev)]
+    x2, w2 = x.clone(), w.clone()
+    qx_us = B.timed_us(lambda i: B.quant_act((x, x2)[i % 2], *qa))
+    qw_us = B.timed_us(lambda i: B.quant_w((w, w2)[i % 2], *qb))
+    res["ffn_8192x18432x7168"] = {
+        "gemm": B.gemm_rec(2 * m * n * k, us, M=m, N=n, K=k, out="bf16", launches=n_gemm),
+        "quant_x_1x128": B.quant_rec(quant_bytes(m, k, "1x128"), qx_us, shape=[m, k], launches=B.launches),
+        "quant_w_128x128": B.quant_rec(quant_bytes(n, k, "128x128"), qw_us, shape=[n, k], launches=B.launches)}
+    del x, w, x2, w2, a, sa, b, sb, y, sets, qa, qb
+    torch.cuda.empty_cache()
+
+    # ---- MoE grouped: 16 experts, seeded counts, X [32768, 7168], W 16 x [4096, 7168]
     counts = synth.expert_counts()
     off_h = synth.offsets_from_counts(counts)
     m, n, k, g = int(off_h[-1]), 4096, 7168, len(counts)
     off = torch.from_numpy(off_h).to(dev)
-    a, sa = codes(m, k), scales(m, k // 128)
-    b, sb = codes(g, n, k), scales(g, n // 128, k // 128)
-    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    us = timed(lambda: check(L.fp8_blockscaled_grouped_gemm(m, n, k, g, vp(off.data_ptr()), vp(a.data_ptr()),
-                                                            vp(sa.data_ptr()), vp(b.data_ptr()),
-                                                            vp(sb.data_ptr()), vp(y.data_ptr()), 0, accum,
-                                                            hs)), 5)
-    out["moe_grouped_32768x4096x7168_g16"] = {"M_total": m, "N": n, "K": k, "G": g,
-                                              "counts": counts.tolist(), "avg_us": round(us, 2),
-                                              "TFLOP/s": round(2 * m * n * k / us / 1e6, 2)}
-    del a, b, y
-    # The MoE workload's quantizers: X [32768, 7168] 1x128, the 16 expert
-    # weights as one [65536, 7168] 128x128 call.
-    x = torch.randn((m, k), device=dev).to(torch.bfloat16)
-    q, s1 = torch.empty((m, k), dtype=torch.uint8, device=dev), torch.empty((m, k // 128), device=dev)
-    us = timed(lambda: check(L.fp8_quant_act_1x128(vp(x.data_ptr()), 0, m, k, k, 0, vp(q.data_ptr()), k,
-                                                   vp(s1.data_ptr()), hs)), 10)
-    byt = m * k * 3 + 4 * m * (k // 128)
-    out["quant_act_1x128_32768x7168"] = {"avg_us": round(us, 2), "GB/s": round(byt / us / 1e3, 1),
-                                         "frac_hbm": round(byt / us / 1e3 / PEAK_HBM_GBPS, 4)}
-    del x, q, s1
-    w = (torch.randn((g * n, k), device=dev) * 0.02).to(torch.bfloat16)
-    q, s2 = torch.empty((g * n, k), dtype=torch.uint8, device=dev), torch.empty((g * n // 128, k // 128), device=dev)
-    us = timed(lambda: check(L.fp8_quant_w_128x128(vp(w.data_ptr()), 0, g * n, k, k, vp(q.data_ptr()), k,
-                                                   vp(s2.data_ptr()), None, 0, None, hs)), 10)
-    byt = g * n * k * 3 + 4 * (g * n // 128) * (k // 128)
-    out["quant_w_128x128_65536x7168"] = {"avg_us": round(us, 2), "GB/s": round(byt / us / 1e3, 1),
-                                         "frac_hbm": round(byt / us / 1e3 / PEAK_HBM_GBPS, 4)}
-    return out
+    x = rand_bf16(torch, dev, (m, k), 1.0, 41)
+    w = rand_bf16(torch, dev, (g * n, k), 0.02, 42)
+    a, sa, b, sb, _ = quantize_pair(x, w)
+    b, sb = b.view(g, n, k), sb.view(g, n // 128, k // 128)
+    y = torch.empty((m, n), dtype=bf, device=dev)
+    sets = rotate([a, sa, b, sb, y])
+    us = B.timed_us(lambda i: B.grouped(off, *sets[i % len(sets)]), n=n_gemm)
+    qx_us = B.timed_us(lambda i: B.quant_act(x, a, sa))
+    qw_us = B.timed_us(lambda i: B.quant_w(w, b.view(g * n, k), sb.view(g * n // 128, k // 128)))
+    res["moe_grouped_32768x4096x7168_g16"] = {
+        "counts": counts.tolist(),
+        "gemm": B.gemm_rec(2 * m * n * k, us, M_total=m, N=n, K=k, G=g, out="bf16", launches=n_gemm),
+        "quant_x_1x128": B.quant_rec(quant_bytes(m, k, "1x128"), qx_us, shape=[m, k], launches=B.launches),
+        "quant_w_128x128": B.quant_rec(quant_bytes(g * n, k, "128x128"), qw_us, shape=[g * n, k],
+                                       launches=B.launches, note="the 16 expert weights as one call")}
+    del x, w, a, sa, b, sb, y, sets
+    torch.cuda.empty_cache()
+
+    # ---- backward: dgrad dX = dY W (B = W^T codes), wgrad dW = X^T dY (both 128x1 along tokens)
+    t, h, f = 8192, 7168, 2048
+    dy = rand_bf16(torch, dev, (t, f), 1e-3, 51)
+    x = rand_bf16(torch, dev, (t, h), 1.0, 52)
+    w = rand_bf16(torch, dev, (f, h), 0.02, 53)
+    g_, sg_, wq, ws, wt = quantize_pair(dy, w, w_t=True)
+    wst = ws.t().contiguous()
+    y = torch.empty((t, h), dtype=bf, device=dev)
+    sets = rotate([g_, sg_, wt, wst, y])
+    dgrad_us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)]), n=n_gemm)
+    del sets, y
+    xt = torch.empty((h, t), dtype=u8, device=dev)
+    sxt = torch.empty((h, t // 128), dtype=f32, device=dev)
+    B.quant_act(x, xt, sxt, tiling=1)
+    gq = torch.empty((t, f), dtype=u8, device=dev)
+    sgq = torch.empty((t, f // 128), dtype=f32, device=dev)
+    gt = torch.empty((f, t), dtype=u8, device=dev)
+    sgt = torch.empty((f, t // 128), dtype=f32, device=dev)
+    B.quant_dual(dy, gq, sgq, gt, sgt)
+    dw = torch.empty((h, f), dtype=f32, device=dev)
+    sets = rotate([xt, sxt, gt, sgt, dw])
+    wgrad_us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)], kind=1), n=n_gemm)
+    del sets
+    dys = [dy] + [dy.clone() for _ in range(B.n_sets(t * f * 2 * 3, cap=16) - 1)]
+    xs = [x, x.clone()]
+    dual_us = B.timed_us(lambda i: B.quant_dual(dys[i % len(dys)], gq, sgq, gt, sgt))
+    xt_us = B.timed_us(lambda i: B.quant_act(xs[i % 2], xt, sxt, tiling=1))
+    ws_ = [w] + [w.clone() for _ in range(B.n_sets(f * h * 2 * 4, cap=16) - 1)]
+    wt_us = B.timed_us(lambda i: B.quant_w(ws_[i % len(ws_)], wq, ws, wt))
+    res["backward_8192x7168x2048"] = {
+        "dgrad_gemm": B.gemm_rec(2 * t * h * f, dgrad_us, M=t, N=h, K=f, out="bf16",
+                                 b="W^T codes from the 128x128 quantizer's transposed copy", launches=n_gemm),
+        "wgrad_gemm": B.gemm_rec(2 * h * f * t, wgrad_us, M=h, N=f, K=t, out="f32", b_scales="row",
+                                 operands="X^T and dY^T, 128x1 tiles along the tokens", launches=n_gemm),
+        "quant_dy_dual": B.quant_rec(quant_bytes(t, f, "dual"), dual_us, shape=[t, f], launches=B.launches,
+                                     note="dY 1x128 (dgrad) and 128x1 transposed (wgrad) from one read"),
+        "quant_x_128x1_t": B.quant_rec(quant_bytes(t, h, "128x1_t"), xt_us, shape=[t, h], launches=B.launches),
+        "quant_w_128x128_t": B.quant_rec(quant_bytes(f, h, "128x128+t"), wt_us, shape=[f, h], launches=B.launches,
+                                         note="codes and transposed codes")}
+    return res
 
 
 def main():
@@ -303,7 +536,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
-    L = fb.lib()
+    B = Bench(torch, fb, args.launches, args.rotate_mib << 20)
 
     print(f"[bench] generating linear workload X[{M},{K}] W[{N},{K}]", file=sys.stderr, flush=True)
     inp = synth.workload_inputs(2)
@@ -312,7 +545,7 @@ def main():
     w0 = torch.from_numpy(wbits.view(np.int16)).view(torch.bfloat16).to(dev)
     out_dtype = torch.bfloat16 if args.out == "bf16" else torch.float32
     set_bytes = x0.numel() * 2 + w0.numel() * 2 + M * N * (2 if args.out == "bf16" else 4)
-    n_sets = max(1, -(-args.rotate_mib * (1 << 20) // set_bytes))
+    n_sets = B.n_sets(set_bytes)
     xs = [x0] + [x0.clone() for _ in range(n_sets - 1)]
     ws = [w0] + [w0.clone() for _ in range(n_sets - 1)]
     ys = [torch.empty((M, N), dtype=out_dtype, device=dev) for _ in range(n_sets)]
@@ -321,24 +554,12 @@ def main():
     b = torch.empty((N, K), dtype=torch.uint8, device=dev)
     sb = torch.empty((N // 128, K // 128), dtype=torch.float32, device=dev)
 
-    stream = torch.cuda.current_stream()
-    hs = ctypes.c_void_p(stream.cuda_stream)
-    vp = ctypes.c_void_p
-    ycode = 0 if args.out == "bf16" else 1
-    accum = fb._ACCUM[args.accum]
-
     def step(i):
-        """Three library calls on `stream`, with prepared arguments (no per-call checks)."""
+        """The step's three library calls on the stream."""
         j = i % n_sets
-        st = L.fp8_quant_act_1x128(vp(xs[j].data_ptr()), 0, M, K, K, 0, vp(a.data_ptr()), K,
-                                   vp(sa.data_ptr()), hs)
-        st |= L.fp8_quant_w_128x128(vp(ws[j].data_ptr()), 0, N, K, K, vp(b.data_ptr()), K,
-                                    vp(sb.data_ptr()), None, 0, None, hs)
-        st |= L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
-                                     vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
-                                     vp(ys[j].data_ptr()), ycode, N, accum, hs)
-        if st:
-            raise RuntimeError(fb.last_error())
+        B.quant_act(xs[j], a, sa)
+        B.quant_w(ws[j], b, sb)
+        B.gemm(a, sa, b, sb, ys[j])
 
     step(0)
     torch.cuda.synchronize()
@@ -355,167 +576,23 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    # Timed region: K steps.  Every event_every-th step also records events
-    # around each of its kernels on the launch stream (the per-kernel and
-    # roofline timings); recording them on every step would add ~10 us of
-    # event overhead to each step's time.
-    # (The first sampled step is not the first timed step, which follows the
-    # synchronization and starts cold.)
-    sampled = [i for i in range(args.steps) if i % args.event_every == args.event_every // 2]
-    if not sampled:
-        sampled = [args.steps - 1]
-    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in sampled}
+    # Timed region: exactly `steps` steps between two events on the launch
+    # stream, synchronized on both sides.
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    def mark(e, k):
-        if e is not None:
-            e[k].record(stream)
-
     torch.cuda.synchronize()
-    start.record(stream)
+    start.record(B.stream)
     for i in range(args.steps):
-        j = i % n_sets
-        e = ev.get(i)
-        mark(e, 0)
-        if L.fp8_quant_act_1x128(vp(xs[j].data_ptr()), 0, M, K, K, 0, vp(a.data_ptr()), K,
-                                 vp(sa.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-        mark(e, 1)
-        if L.fp8_quant_w_128x128(vp(ws[j].data_ptr()), 0, N, K, K, vp(b.data_ptr()), K,
-                                 vp(sb.data_ptr()), None, 0, None, hs):
-            raise RuntimeError(fb.last_error())
-        mark(e, 2)
-        if L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
-                                  vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
-                                  vp(ys[j].data_ptr()), ycode, N, accum, hs):
-            raise RuntimeError(fb.last_error())
-        mark(e, 3)
-    end.record(stream)
+        step(i)
+    end.record(B.stream)
     torch.cuda.synchronize()
-
-    total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    per = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in sampled])
-    avg_ms = per.mean(axis=0)
-    med_ms = np.median(per, axis=0)
-    min_ms = per.min(axis=0)
+    ms_step = start.elapsed_time(end) / args.steps
     qx_bytes, qw_bytes, flops = algorithmic()
-    gemm_tflops = flops / (avg_ms[2] * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if args.accum == "fp32" else PEAK_FP8_TFLOPS
-
-    # For context: the other accumulation mode's GEMM on the same codes.
-    other = 1 - accum
-    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for i in range(5):
-        L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()), vp(b.data_ptr()), K,
-                               vp(sb.data_ptr()), 0, vp(ys[0].data_ptr()), ycode, N, other, hs)
-    g0.record(stream)
-    n_alt = 50
-    for i in range(n_alt):
-        L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()), vp(b.data_ptr()), K,
-                               vp(sb.data_ptr()), 0, vp(ys[i % n_sets].data_ptr()), ycode, N, other, hs)
-    g1.record(stream)
-    torch.cuda.synchronize()
-    alt_us = g0.elapsed_time(g1) / n_alt * 1e3
-    # Further kernels of the path, timed on the rotating X buffers with events
-    # on the launch stream: the dual-orientation quantizer (1x128 and 128x1
-    # transposed from one read) and, for comparison, the 128x1 tiling alone.
-    def timed_us(fn, n=50, warm=5):
-        for i in range(warm):
-            fn(i)
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for i in range(n):
-            fn(i)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / n * 1e3
-
-    qd = torch.empty((M, K), dtype=torch.uint8, device=dev)
-    sd = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
-    qtd = torch.empty((K, M), dtype=torch.uint8, device=dev)
-    std = torch.empty((K, M // 128), dtype=torch.float32, device=dev)
-
-    def dual(i):
-        if L.fp8_quant_act_dual(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, vp(qd.data_ptr()), K,
-                                vp(sd.data_ptr()), vp(qtd.data_ptr()), M, vp(std.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-
-    def t128x1(i):
-        if L.fp8_quant_act_1x128(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 1, vp(qtd.data_ptr()), M,
-                                 vp(std.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-
-    n_deq = 4                       # 4 x (29 MB codes + 59 MB bf16 out) cycled: above the MALL
-    deq_in = [a.clone() for _ in range(n_deq)]
-    deq_out = [torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(n_deq)]
-
-    def dequant(i):
-        if L.fp8_dequant(vp(deq_in[i % n_deq].data_ptr()), M, K, K, vp(sa.data_ptr()), 0,
-                         vp(deq_out[i % n_deq].data_ptr()), 0, K, hs):
-            raise RuntimeError(fb.last_error())
-
-    # The GEMM with its output quantized 1x128 in the epilogue, against the
-    # same result in two launches (float32 GEMM output, then the quantizer).
-    yq = torch.empty((M, N), dtype=torch.uint8, device=dev)
-    ysc = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
-    y32 = torch.empty((M, N), dtype=torch.float32, device=dev)
-
-    def gemm_quant(i):
-        if L.fp8_blockscaled_gemm_quant(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
-                                        vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
-                                        vp(yq.data_ptr()), N, vp(ysc.data_ptr()), accum, hs):
-            raise RuntimeError(fb.last_error())
-
-    def gemm_then_quant(i):
-        if L.fp8_blockscaled_gemm(M, N, K, vp(a.data_ptr()), K, vp(sa.data_ptr()),
-                                  vp(b.data_ptr()), K, vp(sb.data_ptr()), 0,
-                                  vp(y32.data_ptr()), 1, N, accum, hs):
-            raise RuntimeError(fb.last_error())
-        if L.fp8_quant_act_1x128(vp(y32.data_ptr()), 1, M, N, N, 0, vp(yq.data_ptr()), N,
-                                 vp(ysc.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-
-    # Prior-art per-tensor scalings on the same X: current (two passes) and
-    # delayed (one pass, 1024-entry amax history).
-    t_scale = torch.empty((1,), dtype=torch.float32, device=dev)
-    t_amax = torch.empty((1,), dtype=torch.float32, device=dev)
-    t_hist = torch.ones((1024,), dtype=torch.float32, device=dev)
-
-    def tensor_current(i):
-        if L.fp8_quant_tensor(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 0, ctypes.c_float(0.0), None, 0,
-                              vp(a.data_ptr()), K, vp(t_scale.data_ptr()), vp(t_amax.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-
-    def tensor_delayed(i):
-        if L.fp8_quant_tensor(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 0, ctypes.c_float(0.0),
-                              vp(t_hist.data_ptr()), 1024, vp(a.data_ptr()), K, vp(t_scale.data_ptr()),
-                              vp(t_amax.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-
-    tc_us, td_us = timed_us(tensor_current), timed_us(tensor_delayed)
-    gq_us, g2_us = timed_us(gemm_quant), timed_us(gemm_then_quant)
-    # The two step quantizers again, back to back (the per-launch events of
-    # the step add a few microseconds to kernels this short).
-    def quant_x(i):
-        if L.fp8_quant_act_1x128(vp(xs[i % n_sets].data_ptr()), 0, M, K, K, 0, vp(a.data_ptr()), K,
-                                 vp(sa.data_ptr()), hs):
-            raise RuntimeError(fb.last_error())
-
-    def quant_w(i):
-        if L.fp8_quant_w_128x128(vp(ws[i % n_sets].data_ptr()), 0, N, K, K, vp(b.data_ptr()), K,
-                                 vp(sb.data_ptr()), None, 0, None, hs):
-            raise RuntimeError(fb.last_error())
-
-    qx_b2b_us, qw_b2b_us = timed_us(quant_x), timed_us(quant_w)
-    dual_us, t128_us, deq_us = timed_us(dual), timed_us(t128x1), timed_us(dequant)
-    deq_bytes = M * K * (1 + 2) + 4 * M * (K // 128)
-    dual_bytes = M * K * (2 + 1 + 1) + 2 * 4 * M * (K // 128)
-    t128_bytes = qx_bytes
-    qx_gbps = qx_bytes / (avg_ms[0] * 1e-3) / 1e9
-    qw_gbps = qw_bytes / (avg_ms[1] * 1e-3) / 1e9
     value = flops / (ms_step * 1e-3) / 1e12
 
+    print(f"[bench] {ms_step * 1e3:.1f} us per step; timing each kernel over {args.launches} "
+          "back-to-back launches", file=sys.stderr, flush=True)
+    kernels = linear_kernels(B, xs, ws, out_dtype, qx_bytes, qw_bytes, flops)
+    g = kernels["blockscaled_gemm"]
     gemm_src = os.path.join(ROOT, "fp8_block_scaled_05_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(gemm_src, "rb").read()).hexdigest()
     traffic = TRAFFIC["bytes_per_launch"] if TRAFFIC["gemm_sha256"] == sha else None
@@ -535,77 +612,25 @@ def main():
         "data": "synthetic",
         "config": {"workload": "linear layer: quantize X[4096,7168] 1x128 + W[2048,7168] "
                                "128x128, GEMM Y[4096,2048] with FP32 promotion per 128-K block",
-                   "M": M, "N": N, "K": K, "out": args.out, "accum": args.accum,
-                   "buffer_sets": n_sets, "kernel_event_steps": len(sampled)},
+                   "M": M, "N": N, "K": K, "out": args.out, "buffer_sets": n_sets,
+                   "value": "2*M*N*K per whole step (both quantizers + GEMM) over the step time"},
         "device": device_info(torch),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
-                     "traffic": traffic},
-        "kernels": {
-            "quant_act_1x128": {"avg_us": round(qx_b2b_us, 2),
-                                "GB/s": round(qx_bytes / qx_b2b_us / 1e3, 1),
-                                "frac_hbm": round(qx_bytes / qx_b2b_us / 1e3 / PEAK_HBM_GBPS, 4),
-                                "bytes": qx_bytes, "launches": 50,
-                                "in_step_events": {"avg_us": round(avg_ms[0] * 1e3, 2),
-                                                   "median_us": round(med_ms[0] * 1e3, 2),
-                                                   "min_us": round(min_ms[0] * 1e3, 2),
-                                                   "GB/s": round(qx_gbps, 1)},
-                                "note": IN_STEP_NOTE},
-            "quant_w_128x128": {"avg_us": round(qw_b2b_us, 2),
-                                "GB/s": round(qw_bytes / qw_b2b_us / 1e3, 1),
-                                "frac_hbm": round(qw_bytes / qw_b2b_us / 1e3 / PEAK_HBM_GBPS, 4),
-                                "bytes": qw_bytes, "launches": 50,
-                                "in_step_events": {"avg_us": round(avg_ms[1] * 1e3, 2),
-                                                   "median_us": round(med_ms[1] * 1e3, 2),
-                                                   "min_us": round(min_ms[1] * 1e3, 2),
-                                                   "GB/s": round(qw_gbps, 1)},
-                                "note": IN_STEP_NOTE},
-            "blockscaled_gemm": {"accum": args.accum, "mfma": "bf16" if args.accum == "fp32" else "fp8",
-                                 "avg_us": round(avg_ms[2] * 1e3, 2), "median_us": round(med_ms[2] * 1e3, 2),
-                                 "min_us": round(min_ms[2] * 1e3, 2),
-                                 "TFLOP/s": round(gemm_tflops, 2),
-                                 "frac_own_peak": round(gemm_tflops / peak, 4),
-                                 "frac_fp8_peak": round(gemm_tflops / PEAK_FP8_TFLOPS, 4), "flops": flops},
-            "quant_act_dual": {"avg_us": round(dual_us, 2),
-                               "GB/s": round(dual_bytes / dual_us / 1e3, 1),
-                               "frac_hbm": round(dual_bytes / dual_us / 1e3 / PEAK_HBM_GBPS, 4),
-                               "bytes": dual_bytes, "launches": 50,
-                               "note": "X 1x128 and 128x1 (transposed) from one read"},
-            "quant_act_128x1_t": {"avg_us": round(t128_us, 2),
-                                  "GB/s": round(t128_bytes / t128_us / 1e3, 1),
-                                  "frac_hbm": round(t128_bytes / t128_us / 1e3 / PEAK_HBM_GBPS, 4),
-                                  "bytes": t128_bytes, "launches": 50},
-            "dequant_1x128_bf16": {"avg_us": round(deq_us, 2),
-                                   "GB/s": round(deq_bytes / deq_us / 1e3, 1),
-                                   "frac_hbm": round(deq_bytes / deq_us / 1e3 / PEAK_HBM_GBPS, 4),
-                                   "bytes": deq_bytes, "launches": 50},
-            "quant_tensor_current": {"avg_us": round(tc_us, 2),
-                                     "GB/s": round(M * K * 5 / tc_us / 1e3, 1),
-                                     "bytes": M * K * 5, "launches": 50,
-                                     "note": "per-tensor scale (prior art): amax pass + code pass"},
-            "quant_tensor_delayed": {"avg_us": round(td_us, 2),
-                                     "GB/s": round(M * K * 3 / td_us / 1e3, 1),
-                                     "bytes": M * K * 3, "launches": 50,
-                                     "note": "per-tensor scale from a 1024-entry amax history"},
-            "blockscaled_gemm_quant_out": {"accum": args.accum, "avg_us": round(gq_us, 2),
-                                           "TFLOP/s": round(flops / (gq_us * 1e-6) / 1e12, 2),
-                                           "two_launch_us": round(g2_us, 2), "launches": 50,
-                                           "note": "Y quantized 1x128 (E4M3 + scales) in the GEMM "
-                                                   "epilogue vs float32 GEMM then the quantizer"},
-            "blockscaled_gemm_other_accum": {
-                "accum": "fp8_mfma" if args.accum == "fp32" else "fp32", "avg_us": round(alt_us, 2),
-                "TFLOP/s": round(flops / (alt_us * 1e-6) / 1e12, 2), "launches": n_alt},
-        },
+        "roofline": {"bound": "mfma", "achieved": g["TFLOP/s"], "peak": PEAK_FP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": g["frac_fp8_peak"], "traffic": traffic,
+                     "kernel": "blockscaled_gemm", "avg_us": g["avg_us"], "launches": g["launches"],
+                     "frac_bf16_peak": g["frac_bf16_peak"],
+                     "note": "the exact GEMM runs on the bf16 matrix instructions (2.5 PFLOP/s peak)"},
+        "kernels": kernels,
     }
-    if args.extra_workloads:
+    if not args.no_workloads:
         print("[bench] timing the other workload shapes", file=sys.stderr, flush=True)
-        result["extra_workloads"] = extra_workloads(L, fb, torch, dev, hs, accum)
+        result["workloads"] = other_workloads(B)
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xbits, wbits, args.cpu_rows)
-        if args.extra_workloads:
+        if not args.no_workloads:
             print("[bench] timing the CPU oracle on samples of the other workloads", file=sys.stderr, flush=True)
-            result["extra_workloads"]["cpu_baseline"] = extra_cpu_baselines()
+            result["workloads"]["cpu_baseline"] = extra_cpu_baselines()
     print(json.dumps(result), flush=True)
     return 0
 

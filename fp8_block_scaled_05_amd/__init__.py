@@ -21,7 +21,7 @@ import re
 __all__ = [
     "fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
     "fp8_quant_tensor",
-    "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant",
+    "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_fp8mma", "fp8_blockscaled_gemm_quant",
     "fp8_blockscaled_grouped_gemm", "last_error", "version", "lib", "lib_path",
     "Fp8bsError", "STATUS",
 ]
@@ -33,10 +33,8 @@ STATUS = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "ALIGNMENT", 4: "UNSUPPORTED
 BF16, F32 = 0, 1
 TILE_1x128, TILE_128x1_T, TILE_128x128 = 0, 1, 2
 BSCALE_BLOCK128, BSCALE_ROW = 0, 1
-ACCUM_FP32, ACCUM_FP8_MFMA = 0, 1
 FMT_E4M3, FMT_E5M2 = 0, 1
 _FMT = {"e4m3": FMT_E4M3, "e5m2": FMT_E5M2}
-_ACCUM = {"fp32": ACCUM_FP32, "fp8_mfma": ACCUM_FP8_MFMA}
 
 
 class Fp8bsError(RuntimeError):
@@ -63,17 +61,18 @@ def lib():
     L = ctypes.CDLL(path)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
     L.fp8_quant_act_1x128.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
-    L.fp8_quant_w_128x128.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
+    L.fp8_quant_w_128x128.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp]
     L.fp8_quant_act_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
     L.fp8_dequant.argtypes = [vp, i64, i64, i64, vp, i32, vp, i32, i64, vp]
-    L.fp8_quant_tensor.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_float, vp, i32, vp, i64,
+    L.fp8_quant_tensor.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_double, vp, i32, vp, i64,
                                    vp, vp, vp]
-    L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, i32, vp]
-    L.fp8_blockscaled_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i64, vp, i32, vp]
-    L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, i32, vp]
+    L.fp8_blockscaled_gemm.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp]
+    L.fp8_blockscaled_gemm_fp8mma.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp]
+    L.fp8_blockscaled_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i64, vp, vp]
+    L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, vp]
     for f in ("fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
-              "fp8_quant_tensor",
-              "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm"):
+              "fp8_quant_tensor", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_fp8mma",
+              "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int
     L.fp8bs_last_error.restype = ctypes.c_char_p
     L.fp8bs_last_error.argtypes = []
@@ -204,36 +203,32 @@ def fp8_quant_act_dual(x, q=None, scale=None, q_t=None, scale_t=None):
     return q, scale, q_t, scale_t
 
 
-def fp8_quant_w_128x128(w, transpose=False, q=None, scale=None, q_t=None, scale_t=None):
-    """128x128 block quantization; with transpose=True also the transposed codes
-    [cols, rows] and scales [cols/128, rows/128].  Returns (q, scale, q_t, scale_t)."""
+def fp8_quant_w_128x128(w, transpose=False, q=None, scale=None, q_t=None):
+    """128x128 block quantization.  Returns (q [rows, cols], scale
+    [rows/128, cols/128], q_t, scale_t): with transpose=True q_t holds the same
+    codes transposed [cols, rows] and scale_t is scale.t() (a view: a block's
+    scale does not depend on its orientation); otherwise both are None."""
     torch = _torch()
-    _on_gpu(w, q, scale, q_t, scale_t)
+    _on_gpu(w, q, scale, q_t)
     rows, cols = w.shape
     dev = w.device
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
     if scale is None:
         scale = torch.empty((rows // 128, cols // 128), dtype=torch.float32, device=dev)
-    if transpose:
-        if q_t is None:
-            q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
-        if scale_t is None:
-            scale_t = torch.empty((cols // 128, rows // 128), dtype=torch.float32, device=dev)
+    if transpose and q_t is None:
+        q_t = torch.empty((cols, rows), dtype=torch.uint8, device=dev)
     _need(q, (rows, cols), torch.uint8, "q")
     _need(scale, (rows // 128, cols // 128), torch.float32, "scale")
     if q_t is not None:
         _need(q_t, (cols, rows), torch.uint8, "q_t")
-    if scale_t is not None:
-        _need(scale_t, (cols // 128, rows // 128), torch.float32, "scale_t")
-    for t, nm in ((scale, "scale"), (scale_t, "scale_t")):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{nm} must be contiguous")
+    if not scale.is_contiguous():
+        raise ValueError("scale must be contiguous")
     ld_qt = _pitch(q_t, "q_t") if q_t is not None else 0
     _check(lib().fp8_quant_w_128x128(_ptr(w), _dtype_code(w, "w"), rows, cols, _pitch(w, "w"),
                                      _ptr(q), _pitch(q, "q"), _ptr(scale), _ptr(q_t), ld_qt,
-                                     _ptr(scale_t), _stream()))
-    return q, scale, q_t, scale_t
+                                     _stream()))
+    return q, scale, q_t, (scale.t() if q_t is not None else None)
 
 
 def fp8_dequant(q, scale, tiling="1x128", out_dtype=None, y=None):
@@ -288,12 +283,7 @@ def fp8_quant_tensor(x, fmt="e4m3", margin=0.0, history=None, q=None, scale=None
     return q, scale, amax
 
 
-def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None,
-                         accum="fp32"):
-    """y[M, N] = dequant(a) . dequant(b)^T with FP32 promotion per 128-K block.
-
-    accum "fp32" (default) sums each block's exact products in FP32; "fp8_mfma"
-    uses the FP8 matrix instructions (faster, ~14-bit group accumulation)."""
+def _dense_gemm(entry, a, a_scale, b, b_scale, b_kind, out_dtype, y):
     torch = _torch()
     _on_gpu(a, a_scale, b, b_scale, y)
     m, k = a.shape
@@ -314,15 +304,26 @@ def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=No
     for t, nm in ((a_scale, "a_scale"), (b_scale, "b_scale")):
         if not t.is_contiguous():
             raise ValueError(f"{nm} must be contiguous")
-    _check(lib().fp8_blockscaled_gemm(m, n, k, _ptr(a), _pitch(a, "a"), _ptr(a_scale), _ptr(b),
-                                      _pitch(b, "b"), _ptr(b_scale), kind, _ptr(y),
-                                      _dtype_code(y, "y"), _pitch(y, "y"), _ACCUM[accum],
-                                      _stream()))
+    _check(getattr(lib(), entry)(m, n, k, _ptr(a), _pitch(a, "a"), _ptr(a_scale), _ptr(b),
+                                 _pitch(b, "b"), _ptr(b_scale), kind, _ptr(y),
+                                 _dtype_code(y, "y"), _pitch(y, "y"), _stream()))
     return y
 
 
-def fp8_blockscaled_gemm_quant(a, a_scale, b, b_scale, b_kind="block128", yq=None, y_scale=None,
-                               accum="fp32"):
+def fp8_blockscaled_gemm(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None):
+    """y[M, N] = dequant(a) . dequant(b)^T with FP32 promotion per 128-K block
+    (each block's exact products summed in FP32)."""
+    return _dense_gemm("fp8_blockscaled_gemm", a, a_scale, b, b_scale, b_kind, out_dtype, y)
+
+
+def fp8_blockscaled_gemm_fp8mma(a, a_scale, b, b_scale, b_kind="block128", out_dtype=None, y=None):
+    """The same product on the FP8 matrix instructions (faster; their
+    ~14-bit accumulation inside each group of 8 K is outside the accuracy
+    contract of fp8_blockscaled_gemm)."""
+    return _dense_gemm("fp8_blockscaled_gemm_fp8mma", a, a_scale, b, b_scale, b_kind, out_dtype, y)
+
+
+def fp8_blockscaled_gemm_quant(a, a_scale, b, b_scale, b_kind="block128", yq=None, y_scale=None):
     """The GEMM with its float32 output quantized in 1x128 tiles by the GEMM's
     epilogue.  Returns (yq uint8 [M, N], y_scale f32 [M, N/128])."""
     torch = _torch()
@@ -349,12 +350,11 @@ def fp8_blockscaled_gemm_quant(a, a_scale, b, b_scale, b_kind="block128", yq=Non
     _check(lib().fp8_blockscaled_gemm_quant(m, n, k, _ptr(a), _pitch(a, "a"), _ptr(a_scale),
                                             _ptr(b), _pitch(b, "b"), _ptr(b_scale), kind,
                                             _ptr(yq), _pitch(yq, "yq"), _ptr(y_scale),
-                                            _ACCUM[accum], _stream()))
+                                            _stream()))
     return yq, y_scale
 
 
-def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None, y=None,
-                                 accum="fp32"):
+def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None, y=None):
     """Per-group GEMM: group g owns rows [offsets[g], offsets[g+1]) of a and y,
     multiplied by b[g] ([G, N, K] codes, [G, N/128, K/128] scales)."""
     torch = _torch()
@@ -378,5 +378,5 @@ def fp8_blockscaled_grouped_gemm(offsets, a, a_scale, b, b_scale, out_dtype=None
     _need(y, (m, n), y.dtype, "y")
     _check(lib().fp8_blockscaled_grouped_gemm(m, n, k, g, _ptr(offsets), _ptr(a), _ptr(a_scale),
                                               _ptr(b), _ptr(b_scale), _ptr(y),
-                                              _dtype_code(y, "y"), _ACCUM[accum], _stream()))
+                                              _dtype_code(y, "y"), _stream()))
     return y

@@ -122,6 +122,7 @@ extern "C" fp8bs_status fp8_dequant(const uint8_t* q, int64_t rows, int64_t cols
   const int64_t kb = cols / 128;
   const bool blk = tiling == FP8BS_TILE_128x128;
   const bool bf16 = y_dtype == FP8BS_BF16;
+  begin_launch();
 #define FP8BS_L(B, O) hipLaunchKernelGGL((dequant_kernel<B, O, kDeqU>), grid, dim3(256), 0, stream, q, ld_q, scale, kb, \
                                          static_cast<uint32_t>(n_chunks), div, y, ldy)
   if (blk) { if (bf16) FP8BS_L(true, true); else FP8BS_L(true, false); }

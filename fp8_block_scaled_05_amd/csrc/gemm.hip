@@ -18,17 +18,18 @@
 // products in FP32, and every E4M3 value is exact in bf16 (and in f16).  One
 // kernel template serves both block products:
 //
-//  * FP8BS_ACCUM_FP32 (default): E4M3 tiles go from HBM to LDS unchanged
-//    (1 byte per element); each wave widens the 8-byte K slices it feeds to
-//    the matrix core into bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, two
+//  * The exact path (fp8_blockscaled_gemm, the grouped GEMM and the
+//    E4M3-output GEMM): E4M3 tiles go from HBM to LDS unchanged (1 byte
+//    per element); each wave widens the 8-byte K slices it feeds to the
+//    matrix core into bf16 in registers (v_cvt_scalef32_pk_bf16_fp8, two
 //    codes per instruction, exact) and multiplies them with
 //    v_mfma_f32_32x32x16_bf16, eight chained per 128-deep block.  On
 //    E4M3-valued operands it returns bit for bit what the f16 instruction
 //    does; its narrower multipliers draw less power, and sustained matrix
 //    work on this chip is power-limited, so it runs at a higher clock.
-//  * FP8BS_ACCUM_FP8_MFMA: two v_mfma_f32_32x32x64_f8f6f4 per 32x32 output
-//    and K block, straight from the E4M3 bytes; twice the peak rate, with
-//    the accumulation described above.
+//  * fp8_blockscaled_gemm_fp8mma: two v_mfma_f32_32x32x64_f8f6f4 per 32x32
+//    output and K block, straight from the E4M3 bytes; twice the peak rate,
+//    with the accumulation described above (outside the accuracy contract).
 //
 // Structure (dense 256 x 128 output tile, 8 waves of 64 x 64):
 //  * A three-stage LDS ring.  Each stage holds one K block of the A and B
@@ -208,15 +209,18 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
   tile.bscale = args.b_scale;
   tile.n0 = int64_t(tn) * C::BN;
   if constexpr (kGrouped) {
-    // Find the group holding virtual M tile `tm`; offsets are clamped into
-    // [0, M] and a decreasing pair counts as an empty group.
+    // Find the group holding virtual M tile `tm`.  Offsets are clamped into
+    // [0, M], and each group starts no earlier than the previous one ends
+    // (a group whose end lies before that is empty), so the groups' row
+    // ranges never overlap whatever the table holds; for a valid table this
+    // changes nothing.
     int vm = tm, g = 0;
-    int64_t lo = 0, hi = 0;
+    int64_t lo = 0, hi = 0, prev_hi = 0;
     bool found = false;
     for (; g < args.G; ++g) {
-      lo = max(int64_t(0), min(int64_t(args.off[g]), int64_t(args.M)));
-      hi = max(int64_t(0), min(int64_t(args.off[g + 1]), int64_t(args.M)));
-      if (hi < lo) hi = lo;
+      lo = max(prev_hi, min(int64_t(args.off[g]), int64_t(args.M)));
+      hi = max(lo, min(int64_t(args.off[g + 1]), int64_t(args.M)));
+      prev_hi = hi;
       const int cnt = int((hi - lo + C::BM - 1) / C::BM);
       if (vm < cnt) { found = true; break; }
       vm -= cnt;
@@ -286,22 +290,23 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 
   const int64_t rows = min(tile.row_end - tile.row0, int64_t(C::BM));
   const int64_t cols = min(int64_t(args.N) - tile.n0, int64_t(C::BN));
-  const i32x4 rs_a = make_rsrc(args.a + tile.row0 * args.lda, uint64_t(rows) * args.lda);
-  const i32x4 rs_b = make_rsrc(tile.bmat + tile.n0 * args.ldb, uint64_t(cols) * args.ldb);
-  const i32x4 rs_sa = make_rsrc(args.a_scale + tile.row0 * KB, uint64_t(rows) * KB * 4);
-  const i32x4 rs_sb = make_rsrc(tile.bscale + (kRowScale ? tile.n0 * KB : 0),
-                                kRowScale ? uint64_t(cols) * KB * 4 : 4);
   // block128: this tile's row of B scales, read with scalar loads (the
   // constant address space tells the compiler nothing writes it).
   const __attribute__((address_space(4))) float* sb_blk =
       (const __attribute__((address_space(4))) float*)(tile.bscale + (tile.n0 / 128) * KB);
 
-  // Per-lane source offsets of this wave's share of a stage.  Load v of the
-  // wave covers rows 8 (v * NW + wave) .. + 7, lane i taking row + i / 8 and
-  // the logical chunk that lands at physical chunk i % 8.  The swizzle of
-  // those rows does not depend on v (NW is even), so one VGPR offset per
-  // operand serves every v; the row-group term and the K block offset go in
-  // the scalar offset.
+  // Buffer descriptors and per-lane offsets.  The hardware range check of a
+  // raw buffer load covers the VGPR offset only, not the SGPR offset, so
+  // every row-dependent part of an address is in the descriptor base or the
+  // VGPR offset.  Load v of a wave covers rows 8 (v * NW + wave) .. + 7 of the
+  // tile, lane i taking row + i / 8 and the logical chunk that lands at
+  // physical chunk i % 8.  Each v has its own descriptor whose base is the
+  // first row of its row group (8 v NW) and whose size counts only the rows
+  // that exist from there on, so one VGPR offset per operand (lane row times
+  // pitch plus chunk) serves every v: the swizzle of those rows does not
+  // depend on v (NW is even).  The SGPR offset holds only the K block's
+  // kb * 128 < K <= pitch, which stays inside any row that passes the check;
+  // rows that do not exist read as zero.
   constexpr int LA = C::BM / 8 / NW, LB = C::BN / 8 / NW;
   constexpr int kLoadsPerStage = LA + LB;   // tile loads per wave and stage
   static_assert(NW % 2 == 0, "the swizzle argument needs an even wave count");
@@ -309,28 +314,57 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   const int chunk = ((lane & 7) ^ swz(lrow)) << 4;
   const int voff_a = lrow * int(args.lda) + chunk;
   const int voff_b = lrow * int(args.ldb) + chunk;
+  i32x4 rs_a[LA], rs_b[LB];
+#pragma unroll
+  for (int v = 0; v < LA; ++v) {
+    const int64_t r = int64_t(8 * v * NW);
+    rs_a[v] = make_rsrc(args.a + (tile.row0 + r) * args.lda, uint64_t(max(rows - r, int64_t(0))) * args.lda);
+  }
+#pragma unroll
+  for (int v = 0; v < LB; ++v) {
+    const int64_t r = int64_t(8 * v * NW);
+    rs_b[v] = make_rsrc(tile.bmat + (tile.n0 + r) * args.ldb, uint64_t(max(cols - r, int64_t(0))) * args.ldb);
+  }
   // Scale-group loads: load u of this wave covers rows 16 (u * NW + wave) +
-  // lane / 4 and K block 4 g + lane % 4.
+  // lane / 4 and K block 4 g + lane % 4, again with a descriptor per u that
+  // starts at its row group.  The group's K blocks go in the VGPR offset: a
+  // lane whose K block is past the last one reads the next row's first
+  // scales (unused) or, on the last row, zero.
+  constexpr int SUA = C::kScaleLoadsA, SUB = kRowScale ? C::kScaleLoadsB : 1;
   const int voff_s = ((16 * wave + (lane >> 2)) * KB + (lane & 3)) * 4;
+  i32x4 rs_sa[SUA], rs_sb[SUB];
+#pragma unroll
+  for (int u = 0; u < SUA; ++u) {
+    const int64_t r = int64_t(16 * u * NW);
+    rs_sa[u] = make_rsrc(args.a_scale + (tile.row0 + r) * KB, uint64_t(max(rows - r, int64_t(0))) * KB * 4);
+  }
+  if constexpr (kRowScale) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int64_t r = int64_t(16 * u * NW);
+      rs_sb[u] = make_rsrc(tile.bscale + (tile.n0 + r) * KB, uint64_t(max(cols - r, int64_t(0))) * KB * 4);
+    }
+  }
 
   auto load_stage = [&](St& s, int kb) {
 #pragma unroll
     for (int v = 0; v < LA; ++v)
-      dma16(rs_a, lds_addr(&s.a[(v * NW + wave) * 1024]), voff_a, kb * 128 + 8 * v * NW * int(args.lda));
+      dma16(rs_a[v], lds_addr(&s.a[(v * NW + wave) * 1024]), voff_a, kb * 128);
 #pragma unroll
     for (int v = 0; v < LB; ++v)
-      dma16(rs_b, lds_addr(&s.b[(v * NW + wave) * 1024]), voff_b, kb * 128 + 8 * v * NW * int(args.ldb));
+      dma16(rs_b[v], lds_addr(&s.b[(v * NW + wave) * 1024]), voff_b, kb * 128);
   };
   // Scales of K blocks 4 g .. 4 g + 3 into sg[g & 1].
   auto load_scales = [&](int g) {
     Sg& d = sg[g & 1];
+    const int vo = voff_s + g * 16;
 #pragma unroll
-    for (int u = 0; u < C::kScaleLoadsA; ++u)
-      dma4(rs_sa, lds_addr(&d.sa[16 * (u * NW + wave)][0]), voff_s, g * 16 + 16 * u * NW * KB * 4);
+    for (int u = 0; u < SUA; ++u)
+      dma4(rs_sa[u], lds_addr(&d.sa[16 * (u * NW + wave)][0]), vo, 0);
     if constexpr (kRowScale) {
 #pragma unroll
-      for (int u = 0; u < C::kScaleLoadsB; ++u)
-        dma4(rs_sb, lds_addr(&d.sb[16 * (u * NW + wave)][0]), voff_s, g * 16 + 16 * u * NW * KB * 4);
+      for (int u = 0; u < SUB; ++u)
+        dma4(rs_sb[u], lds_addr(&d.sb[16 * (u * NW + wave)][0]), vo, 0);
     }
   };
 
@@ -771,29 +805,24 @@ using CfgSmall = TileCfg<128, 128, 2, 2>;   // 128 x 128 tile, 4 waves of 64 x 6
 // spills there (~40 registers) and this one does not.
 using CfgPair = TileCfg<128, 128, 2, 2, 2, 2>;
 
-template <class C, bool kGrouped>
-void launch_cfg(const GemmArgs& args, bool widen, bool row_scale, int out, uint32_t n_wg,
-                hipStream_t stream) {
+// Launches the kernel variant for one tile configuration; `out` is an
+// OutKind.  Only the variants the entry points can reach are instantiated:
+// E4M3 output exists for the dense exact path only.
+template <class C, bool kWiden, bool kRowScale, bool kGrouped>
+void launch_cfg(const GemmArgs& args, int out, uint32_t n_wg, hipStream_t stream) {
   const dim3 grid(n_wg), block(C::kThreads);
-#define FP8BS_L(F, R, O) hipLaunchKernelGGL((gemm_kernel<C, F, R, O, kGrouped>), grid, block, 0, stream, args)
-#define FP8BS_OUT(F, R)                                                    \
-  if (out == kOutBf16) FP8BS_L(F, R, kOutBf16);                            \
-  else if (out == kOutF32) FP8BS_L(F, R, kOutF32);                         \
-  else if constexpr (!kGrouped) FP8BS_L(F, R, kOutE4M3);
-  if (widen) {
-    if (row_scale) { FP8BS_OUT(true, true) } else { FP8BS_OUT(true, false) }
-  } else {
-    if (row_scale) { FP8BS_OUT(false, true) } else { FP8BS_OUT(false, false) }
+  if (out == kOutBf16) {
+    hipLaunchKernelGGL((gemm_kernel<C, kWiden, kRowScale, kOutBf16, kGrouped>), grid, block, 0, stream, args);
+  } else if (out == kOutF32) {
+    hipLaunchKernelGGL((gemm_kernel<C, kWiden, kRowScale, kOutF32, kGrouped>), grid, block, 0, stream, args);
+  } else if constexpr (kWiden && !kGrouped) {
+    hipLaunchKernelGGL((gemm_kernel<C, kWiden, kRowScale, kOutE4M3, kGrouped>), grid, block, 0, stream, args);
   }
-#undef FP8BS_OUT
-#undef FP8BS_L
 }
 
 // Tile size: the large tile when it still gives at least one workgroup per
 // CU, otherwise the small one.
 constexpr int64_t kNumCU = 256;
-
-bool valid_accum(int32_t accum) { return accum == FP8BS_ACCUM_FP32 || accum == FP8BS_ACCUM_FP8_MFMA; }
 
 }  // namespace
 }  // namespace fp8bs
@@ -805,14 +834,15 @@ namespace {
 
 // Shared by the dense entry points.  `out` is an OutKind; for kOutE4M3, y
 // holds the codes (pitch ldy bytes) and y_scale the [M, N/128] scales.
+// `widen`: the exact path (E4M3 widened to bf16, bf16 matrix instructions);
+// otherwise the FP8 matrix instructions.
 fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const uint8_t* a,
                         int64_t lda, const float* a_scale, const uint8_t* b, int64_t ldb,
                         const float* b_scale, int32_t b_kind, void* y, int out, int64_t ldy,
-                        float* y_scale, int32_t accum, hipStream_t stream) {
+                        float* y_scale, bool widen, hipStream_t stream) {
   if (M < 0 || N < 0 || K < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
   if (b_kind != FP8BS_BSCALE_BLOCK128 && b_kind != FP8BS_BSCALE_ROW)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown b_kind %d", fn, b_kind);
-  if (!valid_accum(accum)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown accum %d", fn, accum);
   if (K % 128 || K < 128) return fail(FP8BS_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 128", fn, (long long)K);
   if (b_kind == FP8BS_BSCALE_BLOCK128 && N % 128)
     return fail(FP8BS_ERR_SHAPE, "%s: block128 B scales need N %% 128 == 0 (N=%lld)", fn, (long long)N);
@@ -843,27 +873,26 @@ fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const u
   args.lda = lda; args.ldb = ldb; args.ldy = ldy;
   args.M = int32_t(M); args.N = int32_t(N); args.KB = int32_t(K / 128);
   args.G = 1;
-  const bool widen = accum == FP8BS_ACCUM_FP32;
   const bool row = b_kind == FP8BS_BSCALE_ROW;
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 127) / 128);
-  if (row && tiles_large >= kNumCU) {
-    args.tiles_m = int32_t((M + 127) / 128);
-    args.tiles_n = int32_t((N + 127) / 128);
-    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgPair, false>(args, widen, row, out, uint32_t(n_wg), stream);
-  } else if (tiles_large >= kNumCU) {
-    args.tiles_m = int32_t((M + 255) / 256);
-    args.tiles_n = int32_t((N + 127) / 128);
-    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgLarge, false>(args, widen, row, out, uint32_t(n_wg), stream);
-  } else {
-    args.tiles_m = int32_t((M + 127) / 128);
-    args.tiles_n = int32_t((N + 127) / 128);
-    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-    launch_cfg<CfgSmall, false>(args, widen, row, out, uint32_t(n_wg), stream);
+  // Per-row B scales on a large output: the paired 128 x 128 tile; block-128
+  // B scales: the 256 x 128 tile; small outputs: the 128 x 128 tile.
+  const int bm = tiles_large >= kNumCU && !row ? 256 : 128;
+  args.tiles_m = int32_t((M + bm - 1) / bm);
+  args.tiles_n = int32_t((N + 127) / 128);
+  const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+  if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
+  begin_launch();
+#define FP8BS_DENSE(W)                                                                         \
+  if (tiles_large >= kNumCU) {                                                                 \
+    if (row) launch_cfg<CfgPair, W, true, false>(args, out, uint32_t(n_wg), stream);           \
+    else launch_cfg<CfgLarge, W, false, false>(args, out, uint32_t(n_wg), stream);             \
+  } else {                                                                                     \
+    if (row) launch_cfg<CfgSmall, W, true, false>(args, out, uint32_t(n_wg), stream);          \
+    else launch_cfg<CfgSmall, W, false, false>(args, out, uint32_t(n_wg), stream);             \
   }
+  if (widen) { FP8BS_DENSE(true) } else { FP8BS_DENSE(false) }
+#undef FP8BS_DENSE
   return check_launch(fn);
 }
 
@@ -873,33 +902,42 @@ fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const u
 extern "C" fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                                              int64_t lda, const float* a_scale, const uint8_t* b,
                                              int64_t ldb, const float* b_scale, int32_t b_kind,
-                                             void* y, int32_t y_dtype, int64_t ldy, int32_t accum,
-                                             hipStream_t stream) {
+                                             void* y, int32_t y_dtype, int64_t ldy, hipStream_t stream) {
   const char* fn = "fp8_blockscaled_gemm";
   if (!valid_dtype(y_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
   return dense_gemm(fn, M, N, K, a, lda, a_scale, b, ldb, b_scale, b_kind, y,
-                    y_dtype == FP8BS_BF16 ? kOutBf16 : kOutF32, ldy, nullptr, accum, stream);
+                    y_dtype == FP8BS_BF16 ? kOutBf16 : kOutF32, ldy, nullptr, true, stream);
+}
+
+extern "C" fp8bs_status fp8_blockscaled_gemm_fp8mma(int64_t M, int64_t N, int64_t K, const uint8_t* a,
+                                                    int64_t lda, const float* a_scale, const uint8_t* b,
+                                                    int64_t ldb, const float* b_scale, int32_t b_kind,
+                                                    void* y, int32_t y_dtype, int64_t ldy,
+                                                    hipStream_t stream) {
+  const char* fn = "fp8_blockscaled_gemm_fp8mma";
+  if (!valid_dtype(y_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
+  return dense_gemm(fn, M, N, K, a, lda, a_scale, b, ldb, b_scale, b_kind, y,
+                    y_dtype == FP8BS_BF16 ? kOutBf16 : kOutF32, ldy, nullptr, false, stream);
 }
 
 extern "C" fp8bs_status fp8_blockscaled_gemm_quant(int64_t M, int64_t N, int64_t K, const uint8_t* a,
                                                    int64_t lda, const float* a_scale, const uint8_t* b,
                                                    int64_t ldb, const float* b_scale, int32_t b_kind,
                                                    uint8_t* yq, int64_t ldyq, float* y_scale,
-                                                   int32_t accum, hipStream_t stream) {
+                                                   hipStream_t stream) {
   return dense_gemm("fp8_blockscaled_gemm_quant", M, N, K, a, lda, a_scale, b, ldb, b_scale, b_kind,
-                    yq, kOutE4M3, ldyq, y_scale, accum, stream);
+                    yq, kOutE4M3, ldyq, y_scale, true, stream);
 }
 
 extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t G,
                                                      const int32_t* off, const uint8_t* a,
                                                      const float* a_scale, const uint8_t* b,
                                                      const float* b_scale, void* y, int32_t y_dtype,
-                                                     int32_t accum, hipStream_t stream) {
+                                                     hipStream_t stream) {
   const char* fn = "fp8_blockscaled_grouped_gemm";
   if (M_total < 0 || N < 0 || K < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
   if (G < 1 || G > 1024) return fail(FP8BS_ERR_INVALID_ARG, "%s: G=%d outside 1..1024", fn, G);
   if (!valid_dtype(y_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown y_dtype %d", fn, y_dtype);
-  if (!valid_accum(accum)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown accum %d", fn, accum);
   if (K % 128 || K < 128) return fail(FP8BS_ERR_SHAPE, "%s: K=%lld must be a positive multiple of 128", fn, (long long)K);
   if (N % 128) return fail(FP8BS_ERR_SHAPE, "%s: N=%lld must be a multiple of 128", fn, (long long)N);
   if (M_total == 0 || N == 0) return FP8BS_OK;
@@ -922,22 +960,17 @@ extern "C" fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N,
   args.bs_group_stride = (N / 128) * (K / 128);
   args.M = int32_t(M_total); args.N = int32_t(N); args.KB = int32_t(K / 128);
   args.G = G;
-  const bool widen = accum == FP8BS_ACCUM_FP32;
   const int out = y_dtype == FP8BS_BF16 ? kOutBf16 : kOutF32;
   // Upper bound on sum_g ceil(m_g / BM): ceil(M_total / BM) + G.
   const int64_t tiles_large = ((M_total + 255) / 256 + G) * (N / 128);
-  if (tiles_large >= 2 * kNumCU) {
-    args.tiles_m = int32_t((M_total + 255) / 256 + G);
-    args.tiles_n = int32_t(N / 128);
-    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgLarge, true>(args, widen, false, out, uint32_t(n_wg), stream);
-  } else {
-    args.tiles_m = int32_t((M_total + 127) / 128 + G);
-    args.tiles_n = int32_t(N / 128);
-    const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
-    if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
-    launch_cfg<CfgSmall, true>(args, widen, false, out, uint32_t(n_wg), stream);
-  }
+  const bool large = tiles_large >= 2 * kNumCU;
+  const int bm = large ? 256 : 128;
+  args.tiles_m = int32_t((M_total + bm - 1) / bm + G);
+  args.tiles_n = int32_t(N / 128);
+  const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
+  if (n_wg > 0x7fffffff) return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles", fn);
+  begin_launch();
+  if (large) launch_cfg<CfgLarge, true, false, true>(args, out, uint32_t(n_wg), stream);
+  else launch_cfg<CfgSmall, true, false, true>(args, out, uint32_t(n_wg), stream);
   return check_launch(fn);
 }

@@ -324,8 +324,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
                                                                  int64_t rows, int64_t cols,
                                                                  uint8_t* __restrict__ q, int64_t ld_q,
                                                                  float* __restrict__ scale,
-                                                                 uint8_t* __restrict__ q_t, int64_t ld_qt,
-                                                                 float* __restrict__ scale_t) {
+                                                                 uint8_t* __restrict__ q_t, int64_t ld_qt) {
   constexpr int kWaves = kThreads / 64;
   constexpr int kRowStep = kThreads / 16;
   constexpr int kRows = 128 / kRowStep;
@@ -375,10 +374,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
         ct[(rr * kCPitch + cc) / 4 + 1] = codes.y;
       }
     }
-    if (t == 0) {
-      scale[bi * col_blocks + bj] = s;
-      if (scale_t) scale_t[bj * (rows / 128) + bi] = s;
-    }
+    if (t == 0) scale[bi * col_blocks + bj] = s;
     __syncthreads();   // red (and ct) are reused by the next block
     if constexpr (kTrans) {
       if (t < 256) {
@@ -589,6 +585,7 @@ extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int6
   if (!aligned4(scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
 
   const bool bf16 = x_dtype == FP8BS_BF16;
+  begin_launch();
   if (!t128x1) {
     const int64_t kb = cols / 128;
     const int64_t n_tiles = rows * kb;
@@ -629,8 +626,7 @@ extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int6
 
 extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,
                                             int64_t ld_w, uint8_t* q, int64_t ld_q, float* scale,
-                                            uint8_t* q_t, int64_t ld_qt, float* scale_t,
-                                            hipStream_t stream) {
+                                            uint8_t* q_t, int64_t ld_qt, hipStream_t stream) {
   const char* fn = "fp8_quant_w_128x128";
   if (!valid_dtype(w_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown w_dtype %d", fn, w_dtype);
   if (rows < 0 || cols < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: negative size", fn);
@@ -646,8 +642,7 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
     st = check_matrix(q_t, cols, ld_qt, rows, 1, "q_t");
     if (st != FP8BS_OK) return st;
   }
-  if (!aligned4(scale) || (scale_t && !aligned4(scale_t)))
-    return fail(FP8BS_ERR_ALIGNMENT, "%s: scales must be 4-byte aligned", fn);
+  if (!aligned4(scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: scale must be 4-byte aligned", fn);
   // One block per workgroup up to FP8BS_W_GRID blocks; beyond that each
   // workgroup takes ceil(blocks / FP8BS_W_GRID) blocks in turn.
   const int64_t n_blocks = (rows / 128) * (cols / 128);
@@ -659,8 +654,9 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
   // Codes (and their transposed copy) up to FP8BS_CACHED_CODE_BYTES are written
   // with ordinary stores, larger outputs stream past the caches.
   const bool cached = rows * cols * (q_t ? 2 : 1) <= int64_t(FP8BS_CACHED_CODE_BYTES);
+  begin_launch();
 #define FP8BS_WL(B, T, NT) hipLaunchKernelGGL((quant_128x128_kernel<B, T, kT, NT>), grid, dim3(kT), 0, stream, \
-                                              w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
+                                              w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt)
 #define FP8BS_WL2(B, T) if (cached) FP8BS_WL(B, T, false); else FP8BS_WL(B, T, true);
   if (bf16 && q_t) { FP8BS_WL2(true, true) }
   else if (bf16) { FP8BS_WL2(true, false) }
@@ -696,6 +692,7 @@ extern "C" fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64
   const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
   constexpr int kT = FP8BS_DUAL_THREADS;
   const bool cached = 2 * rows * cols <= int64_t(FP8BS_CACHED_CODE_BYTES);
+  begin_launch();
 #define FP8BS_DL(B, NT) hipLaunchKernelGGL((quant_dual_kernel<B, kT, true, NT>), grid, dim3(kT), 0, stream, x, ld_x, \
                                            rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
   if (x_dtype == FP8BS_BF16) { if (cached) FP8BS_DL(true, false); else FP8BS_DL(true, true); }

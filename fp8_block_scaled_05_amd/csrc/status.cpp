@@ -18,6 +18,8 @@ fp8bs_status fail(fp8bs_status st, const char* fmt, ...) {
   return st;
 }
 
+void begin_launch() { (void)hipGetLastError(); }
+
 fp8bs_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(FP8BS_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));

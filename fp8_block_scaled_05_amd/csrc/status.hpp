@@ -9,7 +9,12 @@ namespace fp8bs {
 // Records the message for fp8bs_last_error() and returns `st`.
 fp8bs_status fail(fp8bs_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
-// Maps the HIP error state after a launch to a status.
+// Clears the thread's last HIP error before a call's first launch, so that
+// check_launch() reports only errors raised by this call's launches (an
+// earlier failed HIP call on the thread would otherwise show up here).
+void begin_launch();
+
+// Maps the HIP error state after a call's launches to a status.
 fp8bs_status check_launch(const char* what);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

@@ -11,8 +11,13 @@
 // E5M2 (max 57344) is the hybrid recipe's gradient format (German HolySheep
 // article; codingmall "Unified E4M3 Format" says DeepSeek-V3 dropped it).
 //
-// All arithmetic is float32: fl32(amax * fl32(1 + margin)), then an IEEE
-// division by the format maximum, then the correctly rounded x / s.
+// The scale follows the page's arithmetic: the amax comes out of the tensor
+// as a Python float and the margin, the product and the division by the
+// format maximum are Python (binary64) floats, as is the "scale < 1e-6"
+// test.  Here: binary64 (1 + margin), binary64 amax * that, binary64 division
+// by the format maximum, the guard in binary64, then one rounding to float32,
+// the precision in which the scale is stored and x / s is taken (correctly
+// rounded).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -29,16 +34,18 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kE5M2Max = 57344.0f;
-constexpr float kTensorGuard = 1e-6f;   // the page's "scale too small" threshold
+constexpr double kTensorGuard = 1e-6;   // the page's "scale too small" threshold (binary64)
 constexpr int kMaxHistory = 4096;
 
 template <bool kE5M2>
 __device__ __forceinline__ float fmt_max() { return kE5M2 ? kE5M2Max : kE4M3Max; }
 
-__device__ __forceinline__ float tensor_scale_dev(float amax, float widen, float fmax) {
-  const float wide = amax * widen;
-  const float s = wide / fmax;
-  return s < kTensorGuard ? 1.0f : s;
+// widen = 1 + margin in binary64.  Every step is an IEEE binary64 operation
+// (correctly rounded); the result is rounded once to float32.
+__device__ __forceinline__ float tensor_scale_dev(float amax, double widen, double fmax) {
+  const double wide = double(amax) * widen;
+  const double s = wide / fmax;
+  return s < kTensorGuard ? 1.0f : float(s);
 }
 
 // Eight consecutive inputs of one row.
@@ -143,7 +150,7 @@ template <bool kBf16, bool kE5M2, bool kDelayed>
 __global__ __launch_bounds__(kTT) void tensor_quant_kernel(const void* __restrict__ x, int64_t ld_x,
                                                            uint32_t n_chunks, FastDiv per_row,
                                                            const float* __restrict__ src, int hist_len,
-                                                           float widen, uint8_t* __restrict__ q,
+                                                           double widen, uint8_t* __restrict__ q,
                                                            int64_t ld_q, float* __restrict__ scale_out,
                                                            float* __restrict__ amax_out) {
   __shared__ float red[kTT / 64];
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(kTT) void tensor_quant_kernel(const void* __restric
   } else {
     ref = src[0];
   }
-  const float s = tensor_scale_dev(ref, widen, fmt_max<kE5M2>());
+  const float s = tensor_scale_dev(ref, widen, double(fmt_max<kE5M2>()));
   const float r = 1.0f / s;
   if (blockIdx.x == 0 && threadIdx.x == 0) scale_out[0] = s;
   float m = 0.0f;
@@ -219,14 +226,14 @@ __global__ __launch_bounds__(1024) void history_roll_kernel(float* __restrict__ 
 using namespace fp8bs;
 
 extern "C" fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
-                                         int64_t ld_x, int32_t format, float margin, float* history,
+                                         int64_t ld_x, int32_t format, double margin, float* history,
                                          int32_t history_len, uint8_t* q, int64_t ld_q, float* scale,
                                          float* amax, hipStream_t stream) {
   const char* fn = "fp8_quant_tensor";
   if (!valid_dtype(x_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown x_dtype %d", fn, x_dtype);
   if (format != FP8BS_FMT_E4M3 && format != FP8BS_FMT_E5M2)
     return fail(FP8BS_ERR_INVALID_ARG, "%s: unknown format %d", fn, format);
-  if (!(margin >= 0.0f) || !(margin <= 1e6f))
+  if (!(margin >= 0.0) || !(margin <= 1e6))
     return fail(FP8BS_ERR_INVALID_ARG, "%s: margin must be in [0, 1e6]", fn);
   if (history && (history_len < 1 || history_len > kMaxHistory))
     return fail(FP8BS_ERR_INVALID_ARG, "%s: history_len %d outside 1..%d", fn, history_len, kMaxHistory);
@@ -247,9 +254,10 @@ extern "C" fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t
   if (n_chunks > 0xf0000000LL) return fail(FP8BS_ERR_INVALID_ARG, "%s: more than 2^32 chunks", fn);
   const FastDiv div(static_cast<uint32_t>(per_row));
   const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((n_chunks + kTT * kTU - 1) / (kTT * kTU), kTGrid));
-  const float widen = 1.0f + margin;
+  const double widen = 1.0 + margin;
   const bool bf16 = x_dtype == FP8BS_BF16, e5 = format == FP8BS_FMT_E5M2;
 
+  begin_launch();
   hipLaunchKernelGGL(fill_kernel, dim3(1), dim3(64), 0, stream, amax, 0.0f);
 #define FP8BS_Q(B, E, D, SRC, L)                                                                 \
   hipLaunchKernelGGL((tensor_quant_kernel<B, E, D>), dim3(grid), dim3(kTT), 0, stream, x, ld_x, \

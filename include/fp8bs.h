@@ -25,9 +25,14 @@
  *    codes are uint8 (OCP E4M3FN: bias 7, max 448 = 0x7E, no infinity,
  *    S.1111.111 = NaN).  Scales are float32 and dense (row pitch = number of
  *    scale columns).
- *  - Validation is synchronous.  On any non-OK status nothing is enqueued and
- *    no output byte is written; fp8bs_last_error() gives the reason.
- *    Device-side faults surface at the caller's next synchronization.
+ *  - Validation is synchronous.  Every status other than FP8BS_ERR_HIP comes
+ *    from it, and then nothing is enqueued and no output byte is written;
+ *    fp8bs_last_error() gives the reason.  FP8BS_ERR_HIP means the HIP
+ *    runtime refused a launch of this call (any HIP error left over from an
+ *    earlier call on the thread is cleared before the first launch); in a
+ *    call that enqueues several kernels the earlier ones may then already
+ *    be enqueued.  Device-side faults surface at the caller's next
+ *    synchronization.
  *  - Zero rows (or M = 0) is a no-op that returns FP8BS_OK.
  *  - Alignment: every code/input/output pointer 16-byte aligned and every
  *    row pitch a multiple of 16 bytes; scale pointers 4-byte aligned.
@@ -76,24 +81,6 @@ typedef enum fp8bs_bscale_kind {
 } fp8bs_bscale_kind;
 
 /*
- * How the block partials P_kb are accumulated.
- *
- * FP8BS_ACCUM_FP32 (the default): each product of two E4M3 values is exact
- *   and the 128 products of a K block are summed in FP32, so the result
- *   meets |y - exact| <= 2e-5 * sum_k |a_k b_k|.  The codes are widened to
- *   bf16 (exactly) inside the kernel and multiplied on the bf16 matrix cores.
- * FP8BS_ACCUM_FP8_MFMA: the gfx950 FP8 matrix instructions, at twice the
- *   peak rate.  They add products in groups of 8 consecutive K and keep only
- *   the bits down to 2^-13 of each group's largest product (truncating the
- *   rest) before combining the groups in FP32: an error of up to about
- *   7 * 2^-13 of the largest product per group of 8.  This is the limited
- *   matrix-core accumulation precision that the codingmall section "Ökad
- *   ackumuleringsprecision" describes, here inside every instruction, so
- *   promoting more often cannot remove it.
- */
-typedef enum fp8bs_accum { FP8BS_ACCUM_FP32 = 0, FP8BS_ACCUM_FP8_MFMA = 1 } fp8bs_accum;
-
-/*
  * Online activation quantization (codingmall "Finkornig kvantisering" /
  * "Online-kvantisering"; HolySheep (zh) section 2.2, FP8BlockQuantizer).
  *
@@ -123,12 +110,13 @@ fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int64_t rows, i
  * scale:   [rows/128, cols/128] float32.
  * q_t:     optional (may be NULL): the same codes transposed, [cols, rows],
  *          pitch ld_qt >= rows (the B operand of the data-gradient GEMM).
- * scale_t: optional (may be NULL): scale transposed, [cols/128, rows/128].
+ *          A block's scale does not depend on its orientation, so the scale
+ *          grid of q_t is scale transposed ([cols/128, rows/128]): a view of
+ *          scale, not a separate output.
  */
 fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, int64_t cols,
                                  int64_t ld_w, uint8_t* q, int64_t ld_q, float* scale,
-                                 uint8_t* q_t, int64_t ld_qt, float* scale_t,
-                                 hipStream_t stream);
+                                 uint8_t* q_t, int64_t ld_qt, hipStream_t stream);
 
 /*
  * Both activation tilings of one tensor in a single pass over it: what
@@ -176,9 +164,11 @@ fp8bs_status fp8_dequant(const uint8_t* q, int64_t rows, int64_t cols, int64_t l
  * tiles are compared with (one scale for the whole tensor).
  *
  * Current scaling (history == NULL), HolySheep (zh) troubleshooting entry
- * on FP8 overflow, SafeFP8Quantizer.safe_quantize:
- *   amax = max|x|;  s = fl32(fl32(amax * fl32(1 + margin)) / fmt_max);
- *   s = 1 if s < fl32(1e-6);  code = SAT(RNE(fl32(x / s))).
+ * on FP8 overflow, SafeFP8Quantizer.safe_quantize, whose scale arithmetic
+ * is on Python (binary64) floats:
+ *   amax = max|x|;  d = rn64(rn64(amax * rn64(1 + margin)) / fmt_max);
+ *   s = 1 if d < 1e-6 (binary64), else s = fl32(d);
+ *   code = SAT(RNE(fl32(x / s))).
  *   Two passes over x (amax, then the codes).
  * Delayed scaling (history != NULL), HolySheep (zh) FP8Config
  *   (amax_history_len 1024, margin 0): the same formula with amax replaced
@@ -195,11 +185,12 @@ fp8bs_status fp8_dequant(const uint8_t* q, int64_t rows, int64_t cols, int64_t l
  * amax:    DEVICE float[1]: max|x| of this call (also the reduction's
  *          accumulator).
  * history: DEVICE float[history_len] (1..4096) or NULL; updated in place.
- * margin:  >= 0.  Zero rows or columns: nothing is written (the history is
- *          unchanged).  Inputs must be finite.
+ * margin:  binary64 in [0, 1e6] (the page's margin is a Python float, e.g.
+ *          0.1 or 0.15).  Zero rows or columns: nothing is written (the
+ *          history is unchanged).  Inputs must be finite.
  */
 fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t rows, int64_t cols,
-                              int64_t ld_x, int32_t format, float margin, float* history,
+                              int64_t ld_x, int32_t format, double margin, float* history,
                               int32_t history_len, uint8_t* q, int64_t ld_q, float* scale,
                               float* amax, hipStream_t stream);
 
@@ -208,8 +199,11 @@ fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t rows, int6
  * (codingmall "Ökad ackumuleringsprecision"):
  *   y[m,n] = sum_kb  a_scale[m,kb] * bs(n,kb) * P_kb[m,n],
  *   P_kb[m,n] = sum_{k in block kb} e4m3(a[m,k]) * e4m3(b[n,k])
- * where P_kb comes from the matrix cores (see fp8bs_accum) and the promotion
- * is an FP32 multiply-add per K block.
+ * where P_kb comes from the matrix cores and the promotion is an FP32
+ * multiply-add per K block.  Each product of two E4M3 values is exact and
+ * the 128 products of a K block are summed in FP32: the codes are widened
+ * to bf16 (exactly) inside the kernel and multiplied on the bf16 matrix
+ * cores.
  *
  * a:       [M, K] codes, pitch lda >= K;  a_scale [M, K/128] float32.
  * b:       [N, K] codes, pitch ldb >= K (y = A . B^T).
@@ -217,16 +211,34 @@ fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t rows, int6
  *          ROW:      [N, K/128].
  * y:       [M, N] of y_dtype (f32, or bf16 rounded to nearest even), pitch
  *          ldy >= N.
- * accum:   fp8bs_accum (see above).
  * K % 128 == 0 and K >= 128; N % 16 == 0.  M may be any count >= 0.
- * Accuracy with FP8BS_ACCUM_FP32: |y - exact| <= 2e-5 * sum_k |a_k b_k|
- * (+ half a bf16 ulp for bf16 output).
+ * Accuracy: |y - exact| <= 2e-5 * sum_k |a_k b_k| (+ half a bf16 ulp for
+ * bf16 output), where a_k, b_k are the dequantized operands.
  */
 fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
                                   const uint8_t* a, int64_t lda, const float* a_scale,
                                   const uint8_t* b, int64_t ldb, const float* b_scale,
                                   int32_t b_kind, void* y, int32_t y_dtype, int64_t ldy,
-                                  int32_t accum, hipStream_t stream);
+                                  hipStream_t stream);
+
+/*
+ * NOT COVERED BY THE ACCURACY CONTRACT: fp8_blockscaled_gemm computed with
+ * the gfx950 FP8 matrix instructions, at twice their peak rate, for
+ * comparison.  Same arguments, layouts and errors as fp8_blockscaled_gemm.
+ * These instructions add products in groups of 8 consecutive K and keep only
+ * the bits down to 2^-13 of each group's largest product (truncating the
+ * rest) before combining the groups in FP32: an error of up to about
+ * 7 * 2^-13 of the largest product per group of 8, which exceeds
+ * 2e-5 * sum_k |a_k b_k| when one product dominates its group (as the
+ * activations' outliers make it).  This is the limited matrix-core
+ * accumulation that codingmall "Ökad ackumuleringsprecision" describes, here
+ * inside every instruction, so promoting more often cannot remove it.
+ */
+fp8bs_status fp8_blockscaled_gemm_fp8mma(int64_t M, int64_t N, int64_t K,
+                                         const uint8_t* a, int64_t lda, const float* a_scale,
+                                         const uint8_t* b, int64_t ldb, const float* b_scale,
+                                         int32_t b_kind, void* y, int32_t y_dtype, int64_t ldy,
+                                         hipStream_t stream);
 
 /*
  * The block-scaled GEMM with its output quantized in 1x128 tiles inside the
@@ -236,7 +248,7 @@ fp8bs_status fp8_blockscaled_gemm(int64_t M, int64_t N, int64_t K,
  * activation tiles).  Every 128-wide output tile of a row is whole inside
  * one workgroup, so no extra pass over y is needed.
  *
- * Same operands, accum and accuracy as fp8_blockscaled_gemm; N % 128 == 0.
+ * Same operands and accuracy as fp8_blockscaled_gemm; N % 128 == 0.
  * The float32 result y[m,n] (the value fp8_blockscaled_gemm would store
  * with FP8BS_F32) is quantized exactly as fp8_quant_act_1x128 quantizes a
  * float32 input:
@@ -248,7 +260,7 @@ fp8bs_status fp8_blockscaled_gemm_quant(int64_t M, int64_t N, int64_t K,
                                         const uint8_t* a, int64_t lda, const float* a_scale,
                                         const uint8_t* b, int64_t ldb, const float* b_scale,
                                         int32_t b_kind, uint8_t* yq, int64_t ldyq,
-                                        float* y_scale, int32_t accum, hipStream_t stream);
+                                        float* y_scale, hipStream_t stream);
 
 /*
  * Grouped (mixture-of-experts) block-scaled GEMM: group g owns rows
@@ -256,22 +268,25 @@ fp8bs_status fp8_blockscaled_gemm_quant(int64_t M, int64_t N, int64_t K,
  * (HolySheep (zh) MoE module: each expert multiplies its own tokens).
  *
  * off:     DEVICE int32 [G+1], off[0] = 0, nondecreasing, off[G] = M_total.
- *          Not read on the host.  The kernel clamps every offset into
- *          [0, M_total] and treats a decrease as an empty group, so a bad
- *          table cannot cause an out-of-bounds access (its rows are then
- *          simply not computed).
+ *          Not read on the host.  The kernel reads group g's rows as
+ *          [lo_g, hi_g) with lo_g = max(clamp(off[g]), hi_{g-1}) and
+ *          hi_g = max(clamp(off[g+1]), lo_g), clamp() into [0, M_total]
+ *          (hi_{-1} = 0).  For a valid table that is [off[g], off[g+1]); for
+ *          any other table the ranges are still disjoint and inside a, so the
+ *          result is deterministic, no access goes out of bounds, and rows
+ *          covered by no range are not written.
  * a:       [M_total, K] codes (dense, pitch K);  a_scale [M_total, K/128].
  * b:       [G, N, K] codes (dense);  b_scale [G, N/128, K/128] (BLOCK128).
  * y:       [M_total, N] of y_dtype (dense, pitch N).  Rows of empty groups
  *          are not written.
- * accum:   fp8bs_accum, as for fp8_blockscaled_gemm.
+ * Accuracy as for fp8_blockscaled_gemm, per group.
  * N % 128 == 0, K % 128 == 0, K >= 128, 1 <= G <= 1024.
  */
 fp8bs_status fp8_blockscaled_grouped_gemm(int64_t M_total, int64_t N, int64_t K, int32_t G,
                                           const int32_t* off, const uint8_t* a,
                                           const float* a_scale, const uint8_t* b,
                                           const float* b_scale, void* y, int32_t y_dtype,
-                                          int32_t accum, hipStream_t stream);
+                                          hipStream_t stream);
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
 const char* fp8bs_last_error(void);

@@ -23,21 +23,24 @@ int main(void) {
     fprintf(stderr, "last error text: '%s'\n", fp8bs_last_error());
     ++failures;
   }
-  expect("ragged weight", fp8_quant_w_128x128(fake, FP8BS_BF16, 200, 256, 256, (uint8_t*)fake, 256, (float*)fake, NULL, 0, NULL, 0), FP8BS_ERR_SHAPE);
+  expect("ragged weight", fp8_quant_w_128x128(fake, FP8BS_BF16, 200, 256, 256, (uint8_t*)fake, 256, (float*)fake, NULL, 0, 0), FP8BS_ERR_SHAPE);
   expect("gemm K", fp8_blockscaled_gemm(4, 256, 100, (const uint8_t*)fake, 112, (const float*)fake, (const uint8_t*)fake, 112,
                                         (const float*)fake, FP8BS_BSCALE_BLOCK128, (void*)fake, FP8BS_F32, 256,
-                                        FP8BS_ACCUM_FP32, 0), FP8BS_ERR_SHAPE);
+                                        0), FP8BS_ERR_SHAPE);
+  expect("gemm_fp8mma kind", fp8_blockscaled_gemm_fp8mma(4, 256, 256, (const uint8_t*)fake, 256, (const float*)fake,
+                                                         (const uint8_t*)fake, 256, (const float*)fake, 7, (void*)fake,
+                                                         FP8BS_F32, 256, 0), FP8BS_ERR_INVALID_ARG);
   expect("gemm_quant N", fp8_blockscaled_gemm_quant(4, 144, 256, (const uint8_t*)fake, 256, (const float*)fake, (const uint8_t*)fake, 256,
                                                     (const float*)fake, FP8BS_BSCALE_ROW, (uint8_t*)fake, 144, (float*)fake,
-                                                    FP8BS_ACCUM_FP32, 0), FP8BS_ERR_SHAPE);
+                                                    0), FP8BS_ERR_SHAPE);
   expect("grouped G", fp8_blockscaled_grouped_gemm(256, 256, 256, 0, (const int32_t*)fake, (const uint8_t*)fake, (const float*)fake,
                                                    (const uint8_t*)fake, (const float*)fake, (void*)fake, FP8BS_BF16,
-                                                   FP8BS_ACCUM_FP32, 0), FP8BS_ERR_INVALID_ARG);
+                                                   0), FP8BS_ERR_INVALID_ARG);
   expect("dual alignment", fp8_quant_act_dual((const char*)fake + 8, FP8BS_BF16, 128, 128, 128, (uint8_t*)fake, 128, (float*)fake,
                                               (uint8_t*)fake, 128, (float*)fake, 0), FP8BS_ERR_ALIGNMENT);
   expect("dequant tiling", fp8_dequant((const uint8_t*)fake, 4, 128, 128, (const float*)fake, FP8BS_TILE_128x1_T, (void*)fake,
                                        FP8BS_F32, 128, 0), FP8BS_ERR_INVALID_ARG);
-  expect("tensor format", fp8_quant_tensor(fake, FP8BS_BF16, 4, 64, 64, 7, 0.0f, NULL, 0, (uint8_t*)fake, 64, (float*)fake,
+  expect("tensor format", fp8_quant_tensor(fake, FP8BS_BF16, 4, 64, 64, 7, 0.15, NULL, 0, (uint8_t*)fake, 64, (float*)fake,
                                            (float*)fake, 0), FP8BS_ERR_INVALID_ARG);
   if (strstr(fp8bs_version(), "gfx950") == NULL) {
     fprintf(stderr, "version: '%s'\n", fp8bs_version());

@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(L):
     names = fb.header_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128",
                           "fp8_dequant", "fp8_quant_tensor", "fp8_blockscaled_gemm",
-                          "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm",
+                          "fp8_blockscaled_gemm_fp8mma", "fp8_blockscaled_gemm_quant",
+                          "fp8_blockscaled_grouped_gemm",
                           "fp8bs_last_error", "fp8bs_version"}
     for n in names:
         assert hasattr(L, n), n
@@ -53,9 +54,8 @@ def test_quant_act_validation(L):
     assert _act(L, tiling=1, rows=128, cols=8, ldx=8, ldq=64) == INVALID  # q pitch < rows
 
 
-def _w(L, w=A16, dt=0, rows=256, cols=256, ldw=256, q=A16, ldq=256, s=A16, qt=NULL, ldqt=0,
-       st=NULL):
-    return L.fp8_quant_w_128x128(w, dt, rows, cols, ldw, q, ldq, s, qt, ldqt, st, None)
+def _w(L, w=A16, dt=0, rows=256, cols=256, ldw=256, q=A16, ldq=256, s=A16, qt=NULL, ldqt=0):
+    return L.fp8_quant_w_128x128(w, dt, rows, cols, ldw, q, ldq, s, qt, ldqt, None)
 
 
 def test_quant_w_validation(L):
@@ -67,7 +67,6 @@ def test_quant_w_validation(L):
     assert _w(L, qt=A16, ldqt=128) == INVALID                           # ld_qt < rows
     assert _w(L, qt=A16, ldqt=264) == ALIGN
     assert _w(L, s=A16 + 1) == ALIGN
-    assert _w(L, qt=A16, ldqt=256, st=A4 + 1) == ALIGN
 
 
 def _dual(L, x=A16, dt=0, rows=256, cols=384, ldx=384, q=A16, ldq=384, s=A16, qt=A16, ldqt=256,
@@ -118,6 +117,7 @@ def test_quant_tensor_validation(L):
     assert _tq(L, rows=0) == OK and _tq(L, rows=0, x=NULL, q=NULL, s=NULL, a=NULL) == OK
     assert _tq(L, fmt=2) == INVALID and _tq(L, dt=3) == INVALID
     assert _tq(L, margin=-0.1) == INVALID and _tq(L, margin=float("nan")) == INVALID
+    assert _tq(L, margin=2e6) == INVALID
     assert _tq(L, h=A4, hl=0) == INVALID and _tq(L, h=A4, hl=5000) == INVALID
     assert _tq(L, cols=60, ldx=64, ldq=64) == SHAPE
     assert _tq(L, s=NULL) == INVALID and _tq(L, a=NULL) == INVALID and _tq(L, q=NULL) == INVALID
@@ -128,30 +128,32 @@ def test_quant_tensor_validation(L):
 
 
 def _gemm(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, y=A16,
-          ydt=1, ldy=256, accum=0):
-    return L.fp8_blockscaled_gemm(M, N, K, a, lda, sa, b, ldb, sb, kind, y, ydt, ldy, accum, None)
+          ydt=1, ldy=256, entry="fp8_blockscaled_gemm"):
+    return getattr(L, entry)(M, N, K, a, lda, sa, b, ldb, sb, kind, y, ydt, ldy, None)
 
 
-def test_gemm_validation(L):
-    assert _gemm(L, M=0) == OK
-    assert _gemm(L, M=0, a=NULL, y=NULL) == OK
-    assert _gemm(L, K=100, lda=112, ldb=112) == SHAPE
-    assert _gemm(L, K=0) == SHAPE
-    assert _gemm(L, N=144, ldy=144) == SHAPE                            # block128 needs N%128
-    assert _gemm(L, N=24, ldy=32, kind=1) == SHAPE                      # N % 16
-    assert _gemm(L, kind=2) == INVALID and _gemm(L, ydt=9) == INVALID
-    assert _gemm(L, accum=2) == INVALID and _gemm(L, accum=-1) == INVALID
-    assert _gemm(L, M=-3) == INVALID
-    assert _gemm(L, sa=NULL) == INVALID
-    assert _gemm(L, lda=128) == INVALID and _gemm(L, ldy=128) == INVALID
-    assert _gemm(L, a=A16 + 8) == ALIGN and _gemm(L, lda=264) == ALIGN
-    assert _gemm(L, ydt=0, ldy=260) == ALIGN                            # bf16 pitch 520 B
-    assert _gemm(L, sb=A16 + 2) == ALIGN
+@pytest.mark.parametrize("entry", ["fp8_blockscaled_gemm", "fp8_blockscaled_gemm_fp8mma"])
+def test_gemm_validation(L, entry):
+    g = lambda **kw: _gemm(L, entry=entry, **kw)   # noqa: E731
+    assert g(M=0) == OK
+    assert g(M=0, a=NULL, y=NULL) == OK
+    assert g(K=100, lda=112, ldb=112) == SHAPE
+    assert g(K=0) == SHAPE
+    assert g(N=144, ldy=144) == SHAPE                                  # block128 needs N%128
+    assert g(N=24, ldy=32, kind=1) == SHAPE                            # N % 16
+    assert g(kind=2) == INVALID and g(ydt=9) == INVALID
+    assert g(M=-3) == INVALID
+    assert g(sa=NULL) == INVALID
+    assert entry in fb.last_error()
+    assert g(lda=128) == INVALID and g(ldy=128) == INVALID
+    assert g(a=A16 + 8) == ALIGN and g(lda=264) == ALIGN
+    assert g(ydt=0, ldy=260) == ALIGN                                  # bf16 pitch 520 B
+    assert g(sb=A16 + 2) == ALIGN
 
 
 def _gq(L, M=4, N=256, K=256, a=A16, lda=256, sa=A16, b=A16, ldb=256, sb=A16, kind=0, yq=A16,
-        ldyq=256, ys=A16, accum=0):
-    return L.fp8_blockscaled_gemm_quant(M, N, K, a, lda, sa, b, ldb, sb, kind, yq, ldyq, ys, accum, None)
+        ldyq=256, ys=A16):
+    return L.fp8_blockscaled_gemm_quant(M, N, K, a, lda, sa, b, ldb, sb, kind, yq, ldyq, ys, None)
 
 
 def test_gemm_quant_validation(L):
@@ -159,16 +161,15 @@ def test_gemm_quant_validation(L):
     assert _gq(L, N=144, ldyq=144, kind=1) == SHAPE                     # 1x128 output tiles
     assert _gq(L, K=64, lda=64, ldb=64) == SHAPE
     assert _gq(L, ys=NULL) == INVALID and _gq(L, yq=NULL) == INVALID
-    assert _gq(L, kind=3) == INVALID and _gq(L, accum=4) == INVALID
+    assert _gq(L, kind=3) == INVALID
     assert _gq(L, ldyq=128) == INVALID
     assert _gq(L, ldyq=264) == ALIGN and _gq(L, yq=A16 + 8) == ALIGN
     assert _gq(L, ys=A16 + 2) == ALIGN
     assert _gq(L, ldyq=(1 << 40) + 256) == INVALID
 
 
-def _grouped(L, M=256, N=256, K=256, G=4, off=A16, a=A16, sa=A16, b=A16, sb=A16, y=A16, ydt=0,
-             accum=0):
-    return L.fp8_blockscaled_grouped_gemm(M, N, K, G, off, a, sa, b, sb, y, ydt, accum, None)
+def _grouped(L, M=256, N=256, K=256, G=4, off=A16, a=A16, sa=A16, b=A16, sb=A16, y=A16, ydt=0):
+    return L.fp8_blockscaled_grouped_gemm(M, N, K, G, off, a, sa, b, sb, y, ydt, None)
 
 
 def test_grouped_validation(L):
@@ -177,7 +178,7 @@ def test_grouped_validation(L):
     assert _grouped(L, N=144) == SHAPE and _grouped(L, K=64) == SHAPE
     assert _grouped(L, off=NULL) == INVALID
     assert _grouped(L, off=A16 + 2) == ALIGN and _grouped(L, a=A16 + 4) == ALIGN
-    assert _grouped(L, ydt=4) == INVALID and _grouped(L, accum=3) == INVALID
+    assert _grouped(L, ydt=4) == INVALID
 
 
 def test_absurd_pitches_rejected(L):

@@ -25,6 +25,15 @@ def test_algorithmic_counts():
     assert qx == 4096 * 7168 * 3 + 4096 * 56 * 4 == 88_997_888
     assert qw == 2048 * 7168 * 3 + 16 * 56 * 4 == 44_043_776
     assert flops == 2 * 4096 * 2048 * 7168 == 120_259_084_288
+    assert b.quant_bytes(4096, 7168, "1x128") == qx and b.quant_bytes(2048, 7168, "128x128") == qw
+    # the other workloads' quantizers (byte counts of the workload table)
+    assert b.quant_bytes(18432, 7168, "128x128") == 396_393_984
+    assert b.quant_bytes(8192, 7168, "1x128") == 177_995_776
+    assert b.quant_bytes(32768, 7168, "1x128") == 711_983_104
+    assert b.quant_bytes(65536, 7168, "128x128") == 1_409_400_832
+    assert b.quant_bytes(8192, 2048, "1x128") == 50_855_936
+    assert b.quant_bytes(8192, 2048, "dual") == 8192 * 2048 * 4 + 2 * 4 * 8192 * 16
+    assert b.quant_bytes(2048, 7168, "128x128+t") == 2048 * 7168 * 4 + 16 * 56 * 4
 
 
 def test_peaks_are_the_published_ones():
@@ -60,9 +69,10 @@ def test_extra_oracle_samples_run():
     # The oracle leg of --extra-workloads on a reduced sample: every entry
     # names its sample and reports a positive throughput.
     b = _bench()
-    res = b.extra_cpu_baselines(shrink=8)
+    res = b.extra_cpu_baselines(shrink=16)
     assert set(res) == {"ffn_8192x18432x7168", "moe_grouped_32768x4096x7168_g16", "backward_dgrad_wgrad"}
     for v in res.values():
         assert v["kind"] == "oracle" and v["unit"] == "TFLOP/s"
         assert v["value"] > 0 and v["seconds"] > 0 and v["sample"]
-    assert "X[128,7168]" in res["ffn_8192x18432x7168"]["sample"]
+        assert v["cores"]["quantize"] == 1 and v["cores"]["gemm"] >= 1
+    assert "X[64,7168]" in res["ffn_8192x18432x7168"]["sample"]

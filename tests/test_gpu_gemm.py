@@ -123,7 +123,8 @@ def test_dgrad_workload5():
     banner("dgrad workload 5: dY[8192,2048] x W[2048,7168] -> dX, sampled rows and columns")
     a, sa = fb.fp8_quant_act_1x128(dev_bf16(d["dY"]))
     _, _, bt, sbt = fb.fp8_quant_w_128x128(dev_bf16(d["W"]), transpose=True)
-    y = fb.fp8_blockscaled_gemm(a, sa, bt, sbt, "block128", torch.bfloat16)
+    # sbt is scale.t(), a view; the GEMM takes a dense [N/128, K/128] grid
+    y = fb.fp8_blockscaled_gemm(a, sa, bt, sbt.contiguous(), "block128", torch.bfloat16)
     torch.cuda.synchronize()
     rows = synth.sample_rows(a.shape[0], 192, seed=5, must=[0, a.shape[0] - 1])
     blocks = _block_rows(bt.shape[0], 4, seed=55)           # column blocks of W = rows of W^T
@@ -287,24 +288,44 @@ def test_grouped_edges_and_single_group_equals_dense():
     assert torch.equal(y1, yd)
 
 
-def test_grouped_bad_offsets_stay_in_bounds():
-    """A decreasing or out-of-range offset table must not make the kernel touch
-    rows outside [0, M): such groups are clamped (or empty)."""
+@pytest.mark.parametrize("off,ranges", [
+    # group g reads rows [max(clamp(off[g]), end of g-1), max(clamp(off[g+1]), that)):
+    # g0 [0, 200); g1 starts at 200 and ends at 100 -> empty; g2 [200, 300)
+    # (900 clamped to M); g3 and g4 start at 300 -> empty.
+    ([0, 200, 100, 900, -5, 300], {0: (0, 200), 2: (200, 300)}),
+    # g1 = [150, 100) is empty; g2 = [100, 250) is cut to start where g0
+    # ends (150); g3 is empty; g4 = [250, 300).
+    ([0, 150, 100, 250, 250, 300], {0: (0, 150), 2: (150, 250), 4: (250, 300)}),
+    # a table that never reaches M: rows past the last end are not written.
+    ([0, 64, 128, 128, 128, 180], {0: (0, 64), 1: (64, 128), 4: (128, 180)}),
+])
+def test_grouped_bad_offsets_deterministic(off, ranges):
+    """A decreasing, overlapping or out-of-range offset table: every group's
+    rows are clamped into [0, M) and start no earlier than the previous group
+    ends, so the ranges are disjoint (no two workgroups write one row), each
+    written row is that group's product, and rows of no range keep their
+    canary."""
     rng = np.random.default_rng(25)
     n, k, m = 128, 256, 300
-    off = np.array([0, 200, 100, 900, -5, 300], np.int32)
+    off = np.array(off, np.int32)
     a = rng.integers(0, 0x30, size=(m, k), dtype=np.uint8)
     sa = np.ones((m, 2), np.float32)
     b = rng.integers(0, 0x30, size=(5, n, k), dtype=np.uint8)
     sb = np.ones((5, 1, 2), np.float32)
     ybuf = torch.full((m + 2, n), -3.0, dtype=torch.float32, device="cuda")
-    banner("grouped with a bad offset table")
+    banner(f"grouped with a bad offset table {off.tolist()}")
     fb.fp8_blockscaled_grouped_gemm(_dev(off), _dev(a), _dev(sa), _dev(b), _dev(sb),
                                     y=ybuf[1:m + 1])
     torch.cuda.synchronize()
     yb = host(ybuf)
     assert np.all(yb[0] == -3.0) and np.all(yb[-1] == -3.0)
-    assert np.all(np.isfinite(yb[1:m + 1]))
+    y = yb[1:m + 1]
+    written = np.zeros(m, bool)
+    for g, (lo, hi) in ranges.items():
+        ref, bound = oracle.blockscaled_gemm_ref(a[lo:hi], sa[lo:hi], b[g], sb[g])
+        _check_tol(y[lo:hi], ref, bound, "f32", f"group {g} rows {lo}..{hi}")
+        written[lo:hi] = True
+    assert np.all(y[~written] == -3.0)
 
 
 def test_gemm_repeat_bitwise_identical():
@@ -331,9 +352,10 @@ def test_gemm_zero_m_is_noop():
 def test_accumulation_exact_vs_fp8_group_truncation():
     """One large and seven small products in one group of 8 consecutive K:
     256*256 + 7*(2*2) = 65564 is exact in fp32.  The default path (bf16 matrix
-    instructions) must return it; the FP8 matrix instructions keep only bits
-    down to 2^-13 of the group's largest product and return 65536, which is
-    why the default path does not use them."""
+    instructions) must return it; the FP8 matrix instructions
+    (fp8_blockscaled_gemm_fp8mma) keep only bits down to 2^-13 of the group's
+    largest product and return 65536, which is why the contract path does not
+    use them."""
     k = 128
     a = np.zeros((1, k), np.uint8)
     b = np.zeros((16, k), np.uint8)
@@ -343,8 +365,7 @@ def test_accumulation_exact_vs_fp8_group_truncation():
     sb = np.ones((16, 1), np.float32)
     banner("gemm accumulation: 2^16 + 7*4 in one K group")
     y32 = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), "row", torch.float32)
-    y8 = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), "row", torch.float32,
-                                 accum="fp8_mfma")
+    y8 = fb.fp8_blockscaled_gemm_fp8mma(_dev(a), _dev(sa), _dev(b), _dev(sb), "row", torch.float32)
     torch.cuda.synchronize()
     ref, _ = oracle.blockscaled_gemm_ref(a, sa, b, sb, "row")
     assert ref[0, 0] == 65564.0
@@ -389,33 +410,9 @@ def test_fp8_mfma_mode_within_group_model(m, n, k, kind):
         b[(b & 0x7F) == 0x7F] = 0x38
         sb = (rng.random((n // 128 if kind == "block128" else n, k // 128)) + 0.01).astype(np.float32)
     banner(f"gemm fp8_mfma accumulation {m}x{n}x{k} {kind}")
-    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), kind, torch.float32,
-                                accum="fp8_mfma")
+    y = fb.fp8_blockscaled_gemm_fp8mma(_dev(a), _dev(sa), _dev(b), _dev(sb), kind, torch.float32)
     torch.cuda.synchronize()
     ref, bound = oracle.blockscaled_gemm_ref(a, sa, b, sb, kind)
     allow = 2e-5 * bound + _fp8_group_bound(a, sa, b, sb, kind)
     err = np.abs(_y_host(y) - ref)
     assert np.all(err <= allow), f"max err/allow {np.max(err / np.maximum(allow, 1e-300)):.3f}"
-
-
-def test_fp8_mfma_mode_grouped_runs():
-    rng = np.random.default_rng(27)
-    n, k = 128, 256
-    counts = np.array([3, 0, 200])
-    off = synth.offsets_from_counts(counts)
-    m = int(off[-1])
-    a = rng.integers(0, 0x70, size=(m, k), dtype=np.uint8)
-    b = rng.integers(0, 0x70, size=(3, n, k), dtype=np.uint8)
-    sa = np.ones((m, 2), np.float32)
-    sb = np.ones((3, 1, 2), np.float32)
-    banner("grouped gemm fp8_mfma accumulation")
-    y = fb.fp8_blockscaled_grouped_gemm(_dev(off), _dev(a), _dev(sa), _dev(b), _dev(sb),
-                                        torch.float32, accum="fp8_mfma")
-    torch.cuda.synchronize()
-    ref, bound = oracle.grouped_gemm_ref(off, a, sa, b, sb)
-    allow = 2e-5 * bound
-    for e in range(3):
-        lo, hi = off[e], off[e + 1]
-        if hi > lo:
-            allow[lo:hi] += _fp8_group_bound(a[lo:hi], sa[lo:hi], b[e], sb[e], "block128")
-    assert np.all(np.abs(_y_host(y) - ref) <= allow)

@@ -2,7 +2,6 @@
 bit-exact, on the five workloads (full or on row/column/block samples the
 oracle can compute) and on edge cases."""
 
-import os
 
 import numpy as np
 import pytest
@@ -328,23 +327,24 @@ def test_codec_bf16_pairs_exhaustive(part):
         _check_pairs(amax[i:i + 256], fin)
 
 
-@pytest.mark.skipif(os.environ.get("FP8BS_EXHAUSTIVE_F32") != "1",
-                    reason="every fp32 value with |v| <= 448 (~2.2e9) through the f32 encode path; "
-                           "set FP8BS_EXHAUSTIVE_F32=1 (about 2-3 minutes)")
+@pytest.mark.parametrize("part", range(8))
 @pytest.mark.parametrize("sign", [0, 1])
-def test_codec_every_f32_value_unit_scale(sign):
-    """Every fp32 bit pattern of one sign whose magnitude is at most 448, as
-    float32 input rows of 128 whose first element is 448: each tile's scale is
-    exactly 1, so every code is the E4M3 rounding of the value itself.  The
-    patterns are made on the GPU; the oracle encodes each chunk on the host."""
+def test_codec_every_f32_value_unit_scale(sign, part):
+    """Every fp32 bit pattern of one sign whose magnitude is at most 448
+    (2.28e9 patterns over the 16 cases), as float32 input rows of 128 whose
+    first element is 448: each tile's scale is exactly 1, so every code is the
+    E4M3 rounding of the value itself.  Part p of 8 takes every pattern in
+    [p, p + 1) * (top + 1) / 8.  The patterns are made on the GPU; the oracle
+    encodes each chunk on the host."""
     top = int(np.float32(448.0).view(np.uint32))       # magnitudes 0 .. 448 are bit patterns 0 .. top
-    chunk = 127 << 20                                  # 127 values per 128-wide row
-    banner(f"f32 codec sweep, sign {sign}: {top + 1} patterns")
-    for start in range(0, top + 1, chunk):
-        n = min(chunk, top + 1 - start)
+    lo, hi = (top + 1) * part // 8, (top + 1) * (part + 1) // 8
+    chunk = 127 << 19                                  # 127 values per 128-wide row
+    banner(f"f32 codec sweep, sign {sign}, patterns {lo}..{hi - 1}")
+    for start in range(lo, hi, chunk):
+        n = min(chunk, hi - start)
         rows = -(-n // 127)
         bits = torch.arange(start, start + rows * 127, dtype=torch.int64, device="cuda")
-        bits = torch.where(bits > top, torch.full_like(bits, top), bits)     # pad with 448 itself
+        bits = torch.where(bits >= hi, torch.full_like(bits, top), bits)     # pad with 448 itself
         bits = bits | (sign << 31)
         vals = bits.to(torch.int32).view(torch.float32).view(rows, 127)
         x = torch.cat([torch.full((rows, 1), 448.0, device="cuda"), vals], dim=1).contiguous()

@@ -21,7 +21,8 @@ def _run(xd, **kw):
     return host(q), host(s), host(a)
 
 
-@pytest.mark.parametrize("fmt,margin", [("e4m3", 0.0), ("e4m3", 0.15), ("e5m2", 0.0)])
+@pytest.mark.parametrize("fmt,margin", [("e4m3", 0.0), ("e4m3", 0.1), ("e4m3", 0.15), ("e5m2", 0.0),
+                                         ("e5m2", 0.15)])
 def test_current_scaling_workload2_x(fmt, margin):
     bits = inputs(2)["X"][:1024]
     banner(f"per-tensor current {fmt} margin {margin} on X {bits.shape}")
