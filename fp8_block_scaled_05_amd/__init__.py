@@ -19,8 +19,8 @@ import os
 import re
 
 __all__ = [
-    "fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
-    "fp8_quant_tensor",
+    "fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_quant_batch",
+    "fp8_dequant", "fp8_quant_tensor",
     "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_fp8mma", "fp8_blockscaled_gemm_quant",
     "fp8_blockscaled_grouped_gemm", "last_error", "version", "lib", "lib_path",
     "Fp8bsError", "STATUS",
@@ -43,6 +43,16 @@ class Fp8bsError(RuntimeError):
         self.status = status
 
 
+MAX_QUANT_JOBS = 8
+
+
+class QuantJob(ctypes.Structure):
+    """fp8bs_quant_job of include/fp8bs.h."""
+    _fields_ = [("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32), ("tiling", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("ld_x", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("ld_q", ctypes.c_int64), ("scale", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -63,6 +73,7 @@ def lib():
     L.fp8_quant_act_1x128.argtypes = [vp, i32, i64, i64, i64, i32, vp, i64, vp, vp]
     L.fp8_quant_w_128x128.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp]
     L.fp8_quant_act_dual.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, i64, vp, vp]
+    L.fp8_quant_batch.argtypes = [ctypes.POINTER(QuantJob), i32, vp]
     L.fp8_dequant.argtypes = [vp, i64, i64, i64, vp, i32, vp, i32, i64, vp]
     L.fp8_quant_tensor.argtypes = [vp, i32, i64, i64, i64, i32, ctypes.c_double, vp, i32, vp, i64,
                                    vp, vp, vp]
@@ -70,7 +81,8 @@ def lib():
     L.fp8_blockscaled_gemm_fp8mma.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i32, i64, vp]
     L.fp8_blockscaled_gemm_quant.argtypes = [i64, i64, i64, vp, i64, vp, vp, i64, vp, i32, vp, i64, vp, vp]
     L.fp8_blockscaled_grouped_gemm.argtypes = [i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, i32, vp]
-    for f in ("fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_dequant",
+    for f in ("fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128", "fp8_quant_batch",
+              "fp8_dequant",
               "fp8_quant_tensor", "fp8_blockscaled_gemm", "fp8_blockscaled_gemm_fp8mma",
               "fp8_blockscaled_gemm_quant", "fp8_blockscaled_grouped_gemm"):
         getattr(L, f).restype = ctypes.c_int
@@ -229,6 +241,38 @@ def fp8_quant_w_128x128(w, transpose=False, q=None, scale=None, q_t=None):
                                      _ptr(q), _pitch(q, "q"), _ptr(scale), _ptr(q_t), ld_qt,
                                      _stream()))
     return q, scale, q_t, (scale.t() if q_t is not None else None)
+
+
+def fp8_quant_batch(jobs, outs=None):
+    """Several quantizations in one launch.  jobs: list of (x, tiling) with
+    tiling "1x128" (activations) or "128x128" (weights); outs: optional list
+    of (q, scale) per job.  Returns [(q, scale), ...], bit-identical to
+    fp8_quant_act_1x128 / fp8_quant_w_128x128 on each job."""
+    torch = _torch()
+    if len(jobs) > MAX_QUANT_JOBS:
+        raise ValueError(f"at most {MAX_QUANT_JOBS} jobs per call")
+    arr = (QuantJob * max(1, len(jobs)))()
+    res = []
+    for i, (x, tiling) in enumerate(jobs):
+        _on_gpu(x)
+        rows, cols = x.shape
+        tcode = {"1x128": TILE_1x128, "128x128": TILE_128x128}[tiling]
+        sshape = (rows, cols // 128) if tcode == TILE_1x128 else (rows // 128, cols // 128)
+        q, sc = outs[i] if outs is not None else (None, None)
+        if q is None:
+            q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+        if sc is None:
+            sc = torch.empty(sshape, dtype=torch.float32, device=x.device)
+        _on_gpu(q, sc)
+        _need(q, (rows, cols), torch.uint8, "q")
+        _need(sc, sshape, torch.float32, "scale")
+        if not sc.is_contiguous():
+            raise ValueError("scale must be contiguous")
+        arr[i] = QuantJob(x.data_ptr(), _dtype_code(x, "x"), tcode, rows, cols, _pitch(x, "x"),
+                          q.data_ptr(), _pitch(q, "q"), sc.data_ptr())
+        res.append((q, sc))
+    _check(lib().fp8_quant_batch(arr, len(jobs), _stream()))
+    return res
 
 
 def fp8_dequant(q, scale, tiling="1x128", out_dtype=None, y=None):

@@ -240,17 +240,6 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
 // Output element types of the GEMM.
 enum OutKind : int { kOutF32 = 0, kOutBf16 = 1, kOutE4M3 = 2 };
 
-template <int kOut>
-__device__ __forceinline__ void store4(void* y, int64_t off, float v0, float v1, float v2, float v3) {
-  if constexpr (kOut == kOutBf16) {
-    const uint32_t lo = f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16);
-    const uint32_t hi = f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16);
-    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + off) = make_uint2(lo, hi);
-  } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + off) = make_float4(v0, v1, v2, v3);
-  }
-}
-
 // Makes x live in registers here: values feeding it must be computed first.
 __device__ __forceinline__ void keep_in_vgprs(v16f& x) { asm volatile("" : "+v"(x)); }
 
@@ -578,6 +567,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     }
   };
 
+  // A grouped wave with no rows of its expert (see below) skips the matrix
+  // work but still takes every barrier, the epilogue's included.
+  bool idle = false;
   if constexpr (C::kStages == 2) {
     // Two-stage ring: block kb is in stage kb % 2.  The barrier of step kb
     // (before its last slice) waits for block kb + 1 and, since every read of
@@ -612,8 +604,8 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     // A wave whose TM-row slab lies entirely past its group's last row (in
     // an expert's tail tile) has nothing to multiply.  It issues its share
     // of the stage and scale loads and takes the same barriers, with the
-    // same waits, as the main loop below, then leaves: no barrier follows
-    // the last one here, and its rows are not stored.
+    // same waits, as the main loop below, then goes on to the epilogue,
+    // whose barriers it takes too; its rows are not stored.
     if (int64_t(wm) * C::TM >= rows) {
       load_scales(0);
       load_stage(st0, 0);
@@ -629,9 +621,10 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
         if (kb + 2 < KB) wait_and_barrier<kLoadsPerStage>();
         else if (kb + 1 < KB) wait_and_barrier<0>();
       }
-      return;
+      idle = true;
     }
   }
+  if (!idle) {
   // Prologue: scales of K blocks 0..3 and K blocks 0 and 1 in flight,
   // block 0 visible, its slice 0 read.
   load_scales(0);
@@ -701,13 +694,14 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   FP8BS_STEP_TAIL(A, st0, st1, st2, kb + 3)
 #undef FP8BS_STEP_FULL
 #undef FP8BS_STEP_TAIL
+  }  // !idle
   }
 
   // kLag: the last block, K block KB - 1, may still be pending: in
   // p[(KB - 1) & 1] on the two-stage ring; on the three-stage ring in p[0]
   // after an A step and in p[1] after a B step.
   if constexpr (kLag) {
-    const int last = C::kStages == 2 ? ((KB - 1) & 1) : ((KB - 1) % 3);
+    const int last = idle ? -1 : (C::kStages == 2 ? ((KB - 1) & 1) : ((KB - 1) % 3));
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -778,20 +772,66 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
             *reinterpret_cast<const uint4*>(ct + rl * kPitch + 16 * ch);
     }
   } else {
-    // Epilogue: four consecutive columns per store.
+    // Epilogue through LDS.  A lane's accumulators hold four consecutive
+    // columns of 32 different rows per register group, so direct stores
+    // would scatter each instruction over 32 rows.  Instead each wave writes
+    // its converted values row-major into LDS (rows [0, BM/2) in the first
+    // stage buffer, the rest in the second; row pitch = the round's columns
+    // plus 16 bytes), and the workgroup then stores whole rows with 16-byte
+    // chunks, consecutive threads on consecutive addresses.  bf16 output
+    // takes the whole tile in one round; f32 output one wave column (TN
+    // columns) per round.  Every tile of this configuration is one wave of
+    // workgroups on the chip, so these stores are not hidden behind other
+    // tiles' matrix work: whole-line writes keep them short.
+    constexpr int kElt = kOut == kOutBf16 ? 2 : 4;
+    constexpr int kRounds = kOut == kOutBf16 ? 1 : C::WN;
+    constexpr int kCols = C::BN / kRounds;            // columns per round
+    constexpr int kPitch = kCols * kElt + 16;         // LDS row pitch (bytes)
+    constexpr int kHalf = C::BM / 2;
+    static_assert(kHalf * kPitch <= int(sizeof(St)), "half the output tile fits a stage buffer");
+    static_assert(C::TM <= kHalf && kHalf % C::TM == 0, "a wave's rows lie in one half");
+    constexpr int kChunks = kCols * kElt / 16;        // 16-byte chunks per row and round
+    uint8_t* const lo_half = reinterpret_cast<uint8_t*>(&st0);
+    uint8_t* const hi_half = reinterpret_cast<uint8_t*>(&st1);
+    __syncthreads();   // every wave is past its last read of the stages
 #pragma unroll
-    for (int i = 0; i < SM; ++i) {
-      const int64_t row = tile.row0 + arow0 + 32 * i;
-      if (row >= tile.row_end) continue;
+    for (int rd = 0; rd < kRounds; ++rd) {
+      if (kRounds == 1 || wn == rd) {
+        const int c0 = kRounds == 1 ? wn * C::TN : 0;   // the wave's first column in this round
 #pragma unroll
-      for (int j = 0; j < SN; ++j)
+        for (int i = 0; i < SM; ++i) {
+          const int rl = arow0 + 32 * i;
+          uint8_t* rowp = (rl < kHalf ? lo_half : hi_half) + (rl % kHalf) * kPitch;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t col = tile.n0 + wn * C::TN + 32 * j + 8 * g + 4 * hk;
-          if (col < args.N)
-            store4<kOut>(args.y, row * args.ldy + col, acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                         acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          for (int j = 0; j < SN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int cl = c0 + 32 * j + 8 * g + 4 * hk;
+              const float v0 = acc[i][j][4 * g], v1 = acc[i][j][4 * g + 1];
+              const float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
+              if constexpr (kOut == kOutBf16) {
+                *reinterpret_cast<uint2*>(rowp + cl * 2) =
+                    make_uint2(f32_to_bf16_rne(v0) | (f32_to_bf16_rne(v1) << 16),
+                               f32_to_bf16_rne(v2) | (f32_to_bf16_rne(v3) << 16));
+              } else {
+                *reinterpret_cast<float4*>(rowp + cl * 4) = make_float4(v0, v1, v2, v3);
+              }
+            }
         }
+      }
+      __syncthreads();
+      const int64_t col0 = tile.n0 + (kRounds == 1 ? 0 : rd * kCols);
+      uint8_t* ybase = static_cast<uint8_t*>(args.y);
+#pragma unroll 4
+      for (int c = threadIdx.x; c < C::BM * kChunks; c += C::kThreads) {
+        const int rl = c / kChunks, ch = c % kChunks;
+        const int64_t row = tile.row0 + rl;
+        const int64_t col = col0 + ch * (16 / kElt);
+        if (row < tile.row_end && col < args.N)
+          *reinterpret_cast<uint4*>(ybase + (row * args.ldy + col) * kElt) =
+              *reinterpret_cast<const uint4*>((rl < kHalf ? lo_half : hi_half) + (rl % kHalf) * kPitch + ch * 16);
+      }
+      if (rd + 1 < kRounds) __syncthreads();   // the next round rewrites the buffers
     }
   }
 }

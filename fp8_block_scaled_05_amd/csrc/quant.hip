@@ -550,6 +550,154 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Several quantization jobs in one launch (fp8_quant_batch): each job is a
+// 1x128 activation quantization or a 128x128 weight quantization, computed
+// exactly as its single call does (bit-identical outputs).  The launch grid
+// is the concatenation of the jobs' workgroups; a workgroup finds its job
+// from the jobs' first workgroup indices (uniform per workgroup) and runs
+// that job's code: 32 1x128 tiles (4 waves x 4 tiles x kBatchU steps) or
+// one 128x128 block (thread t holds columns 8 (t % 16) .. + 7 of rows
+// t / 16 + 16 p, p < 8).  One launch pays one fill and drain of the machine
+// for all the jobs; the host puts the 128x128 jobs first, so that their
+// heavier workgroups start first instead of trailing.
+constexpr int kMaxBatchJobs = 8;
+// 1x128 steps per wave.  At the lower occupancy of this kernel, four steps
+// keep more loads in flight than the single kernel's two: X [4096, 7168]
+// 1x128 + W [2048, 7168] 128x128 took 23.2 us with 3 or 4 steps, 23.8 us
+// with 2, 24.4 with 6 and 25.0 with 8 (alternated on one box).
+#ifndef FP8BS_BATCH_U
+#define FP8BS_BATCH_U 4
+#endif
+constexpr int kBatchU = FP8BS_BATCH_U;
+
+enum BatchKind : int32_t {
+  kAct1x128Bf16 = 0, kAct1x128F32 = 1,
+  kW128Bf16 = 2, kW128Bf16NT = 3, kW128F32 = 4, kW128F32NT = 5
+};
+
+struct BatchJob {
+  const void* x;
+  uint8_t* q;
+  float* scale;
+  int64_t ld_x, ld_q;
+  uint32_t n_units;      // 1x128: tiles; 128x128: blocks
+  uint32_t col_blocks;   // 128-column blocks per row (128x128)
+  FastDiv per_row;       // 1x128: tiles per row
+  uint32_t first_wg;
+  int32_t kind;
+};
+
+struct BatchArgs {
+  BatchJob job[kMaxBatchJobs];
+  int32_t n;
+};
+
+// 1x128 tiles base .. of one job for global wave `wave` (the body of
+// quant_1x128_kernel).
+template <bool kBf16, int kU>
+__device__ __forceinline__ void act_tiles(const BatchJob& jb, uint32_t wave) {
+  constexpr int kElt = kBf16 ? 2 : 4;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t sub = lane & 15u;
+  const uint32_t slot = lane >> 4;
+  const uint32_t base = wave * (4u * kU);
+  const uint32_t n_tiles = jb.n_units;
+  float v[kU][8];
+  uint32_t tile[kU], row[kU], kb[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    uint32_t t = base + 4u * u + slot;
+    tile[u] = t;
+    t = t < n_tiles ? t : n_tiles - 1;          // clamp: every lane stays active
+    row[u] = jb.per_row.div(t);
+    kb[u] = t - row[u] * jb.per_row.d;
+    const char* p = static_cast<const char*>(jb.x) +
+                    (int64_t(row[u]) * jb.ld_x + int64_t(kb[u]) * 128 + sub * 8) * kElt;
+    load8<kBf16>(p, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const float s = tile_scale(row16_max(absmax8(v[u])));
+    const float r = 1.0f / s;
+    const uint2 codes = encode8<kBf16>(v[u], s, r);
+    if (tile[u] < n_tiles) {
+      store_codes8(jb.q + int64_t(row[u]) * jb.ld_q + int64_t(kb[u]) * 128 + sub * 8, codes);
+      if (sub == 0) store_scale(&jb.scale[tile[u]], s);
+    }
+  }
+}
+
+// One 128x128 block of one job (the body of quant_128x128_kernel without
+// the transposed copy), 256 threads.
+template <bool kBf16, bool kNT>
+__device__ __forceinline__ void w_block(const BatchJob& jb, uint32_t blk, float* red) {
+  constexpr int kRowStep = 16, kRows = 8;
+  const int t = threadIdx.x;
+  const int cc = (t & 15) * 8;
+  const int rbase = t >> 4;
+  const uint32_t bi = blk / jb.col_blocks, bj = blk - bi * jb.col_blocks;
+  const int64_t r0 = int64_t(bi) * 128, c0 = int64_t(bj) * 128;
+  RawRows<kBf16, kRows> raw;
+  load_rows<kBf16, kRows, kRowStep>(raw, jb.x, jb.ld_x, r0, c0, rbase, cc);
+  // The raw input stays in registers; it is widened to float32 once for the
+  // maximum and again for the codes (cheaper than holding 64 floats).
+  float m = 0.0f;
+#pragma unroll
+  for (int p = 0; p < kRows; ++p) {
+    float v[8];
+    unpack8<kBf16>(raw.d[p], v);
+    m = fmaxf(m, absmax8(v));
+  }
+  m = wave_max(m);
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = tile_scale(m);
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int p = 0; p < kRows; ++p) {
+    float v[8];
+    unpack8<kBf16>(raw.d[p], v);
+    store_codes8<kNT>(jb.q + (r0 + rbase + kRowStep * p) * jb.ld_q + c0 + cc, encode8<kBf16>(v, s, r));
+  }
+  if (t == 0) jb.scale[blk] = s;
+}
+
+// kF32: the batch holds float32 inputs (their code paths need more
+// registers, so batches of bf16 inputs get a variant without them).  The
+// occupancy floors (6 and 5 waves per SIMD) are the highest at which each
+// variant compiles without spills: the 1x128 jobs keep many loads in flight.
+#ifndef FP8BS_BATCH_OCC
+#define FP8BS_BATCH_OCC 6
+#endif
+template <bool kF32>
+__global__ __launch_bounds__(256, kF32 ? 5 : FP8BS_BATCH_OCC) void quant_batch_kernel(const BatchArgs args) {
+  __shared__ float red[4];
+  const uint32_t wg = blockIdx.x;
+  int j = 0;
+  while (j + 1 < args.n && wg >= args.job[j + 1].first_wg) ++j;
+  const BatchJob& jb = args.job[j];
+  const uint32_t local = wg - jb.first_wg;
+  const uint32_t wave = local * 4u + (threadIdx.x >> 6);
+  if constexpr (kF32) {
+    switch (jb.kind) {
+      case kAct1x128Bf16: act_tiles<true, kBatchU>(jb, wave); break;
+      case kAct1x128F32: act_tiles<false, kBatchU>(jb, wave); break;
+      case kW128Bf16: w_block<true, false>(jb, local, red); break;
+      case kW128Bf16NT: w_block<true, true>(jb, local, red); break;
+      case kW128F32: w_block<false, false>(jb, local, red); break;
+      default: w_block<false, true>(jb, local, red); break;
+    }
+  } else {
+    switch (jb.kind) {
+      case kAct1x128Bf16: act_tiles<true, kBatchU>(jb, wave); break;
+      case kW128Bf16: w_block<true, false>(jb, local, red); break;
+      default: w_block<true, true>(jb, local, red); break;
+    }
+  }
+}
+
 fp8bs_status check_matrix(const void* p, int64_t rows, int64_t ld, int64_t cols, int elt, const char* name) {
   if (ld < cols) return fail(FP8BS_ERR_INVALID_ARG, "%s: pitch %lld < columns %lld", name, (long long)ld, (long long)cols);
   if (!sane_matrix(rows, ld, elt))
@@ -698,5 +846,72 @@ extern "C" fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64
   if (x_dtype == FP8BS_BF16) { if (cached) FP8BS_DL(true, false); else FP8BS_DL(true, true); }
   else { if (cached) FP8BS_DL(false, false); else FP8BS_DL(false, true); }
 #undef FP8BS_DL
+  return check_launch(fn);
+}
+
+extern "C" fp8bs_status fp8_quant_batch(const fp8bs_quant_job* jobs, int32_t n_jobs, hipStream_t stream) {
+  const char* fn = "fp8_quant_batch";
+  static_assert(FP8BS_MAX_QUANT_JOBS == kMaxBatchJobs, "job capacity");
+  if (n_jobs < 0 || n_jobs > FP8BS_MAX_QUANT_JOBS)
+    return fail(FP8BS_ERR_INVALID_ARG, "%s: n_jobs=%d outside 0..%d", fn, n_jobs, FP8BS_MAX_QUANT_JOBS);
+  if (n_jobs > 0 && !jobs) return fail(FP8BS_ERR_INVALID_ARG, "%s: null job array", fn);
+  // Validate every job before anything is launched, exactly as the single
+  // calls validate their arguments.
+  for (int32_t i = 0; i < n_jobs; ++i) {
+    const fp8bs_quant_job& jb = jobs[i];
+    if (!valid_dtype(jb.x_dtype)) return fail(FP8BS_ERR_INVALID_ARG, "%s: job %d: unknown x_dtype %d", fn, i, jb.x_dtype);
+    if (jb.tiling != FP8BS_TILE_1x128 && jb.tiling != FP8BS_TILE_128x128)
+      return fail(FP8BS_ERR_INVALID_ARG, "%s: job %d: tiling %d is not 1x128 or 128x128", fn, i, jb.tiling);
+    if (jb.rows < 0 || jb.cols < 0) return fail(FP8BS_ERR_INVALID_ARG, "%s: job %d: negative size", fn, i);
+    if (jb.cols % 128 || (jb.tiling == FP8BS_TILE_128x128 && jb.rows % 128))
+      return fail(FP8BS_ERR_SHAPE, "%s: job %d: rows %lld / cols %lld not whole tiles", fn, i,
+                  (long long)jb.rows, (long long)jb.cols);
+    if (jb.rows == 0 || jb.cols == 0) continue;
+    if (!jb.x || !jb.q || !jb.scale) return fail(FP8BS_ERR_INVALID_ARG, "%s: job %d: null pointer", fn, i);
+    fp8bs_status st = check_matrix(jb.x, jb.rows, jb.ld_x, jb.cols, elem_size(jb.x_dtype), "x");
+    if (st != FP8BS_OK) return fail(st, "%s: job %d: %s", fn, i, fp8bs_last_error());
+    st = check_matrix(jb.q, jb.rows, jb.ld_q, jb.cols, 1, "q");
+    if (st != FP8BS_OK) return fail(st, "%s: job %d: %s", fn, i, fp8bs_last_error());
+    if (!aligned4(jb.scale)) return fail(FP8BS_ERR_ALIGNMENT, "%s: job %d: scale must be 4-byte aligned", fn, i);
+    const int64_t units = jb.tiling == FP8BS_TILE_1x128 ? jb.rows * (jb.cols / 128)
+                                                       : (jb.rows / 128) * (jb.cols / 128);
+    if (units > 0x7fffffffLL) return fail(FP8BS_ERR_INVALID_ARG, "%s: job %d: more than 2^31 tiles", fn, i);
+  }
+  // 128x128 jobs first (heavier workgroups start first), then 1x128 jobs.
+  BatchArgs args{};
+  int64_t total = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int32_t i = 0; i < n_jobs; ++i) {
+      const fp8bs_quant_job& jb = jobs[i];
+      const bool w = jb.tiling == FP8BS_TILE_128x128;
+      if (w != (pass == 0) || jb.rows == 0 || jb.cols == 0) continue;
+      BatchJob& d = args.job[args.n++];
+      d.x = jb.x; d.q = jb.q; d.scale = jb.scale; d.ld_x = jb.ld_x; d.ld_q = jb.ld_q;
+      d.first_wg = uint32_t(total);
+      const bool bf16 = jb.x_dtype == FP8BS_BF16;
+      if (w) {
+        d.n_units = uint32_t((jb.rows / 128) * (jb.cols / 128));
+        d.col_blocks = uint32_t(jb.cols / 128);
+        const bool nt = jb.rows * jb.cols > int64_t(FP8BS_CACHED_CODE_BYTES);
+        d.kind = bf16 ? (nt ? kW128Bf16NT : kW128Bf16) : (nt ? kW128F32NT : kW128F32);
+        total += d.n_units;
+      } else {
+        d.n_units = uint32_t(jb.rows * (jb.cols / 128));
+        d.per_row = FastDiv(uint32_t(jb.cols / 128));
+        d.kind = bf16 ? kAct1x128Bf16 : kAct1x128F32;
+        total += (int64_t(d.n_units) + 4 * 4 * kBatchU - 1) / (4 * 4 * kBatchU);
+      }
+      if (total > 0x7fffffffLL) return fail(FP8BS_ERR_INVALID_ARG, "%s: more than 2^31 workgroups", fn);
+    }
+  }
+  if (total == 0) return FP8BS_OK;
+  bool any_f32 = false;
+  for (int i = 0; i < args.n; ++i)
+    any_f32 |= args.job[i].kind == kAct1x128F32 || args.job[i].kind == kW128F32 || args.job[i].kind == kW128F32NT;
+  begin_launch();
+  if (any_f32)
+    hipLaunchKernelGGL(quant_batch_kernel<true>, dim3(uint32_t(total)), dim3(256), 0, stream, args);
+  else
+    hipLaunchKernelGGL(quant_batch_kernel<false>, dim3(uint32_t(total)), dim3(256), 0, stream, args);
   return check_launch(fn);
 }

@@ -119,6 +119,42 @@ fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int64_t rows, i
                                  uint8_t* q_t, int64_t ld_qt, hipStream_t stream);
 
 /*
+ * Several quantization jobs in one launch: each job is what
+ * fp8_quant_act_1x128 computes with FP8BS_TILE_1x128, or what
+ * fp8_quant_w_128x128 computes without the transposed copy, with the same
+ * arguments (codingmall "Finkornig kvantisering": 1x128 activation tiles and
+ * 128x128 weight blocks, each with its own scale; HolySheep (zh) section 2.2
+ * rule per tile).  Outputs are bit-identical to the single calls.  One launch
+ * pays the machine's fill and drain once for all jobs: a linear layer's
+ * activations and weight, or the separate weights of several experts.
+ *
+ * jobs:    HOST array of n_jobs descriptors, read during the call only.
+ *   x, x_dtype, rows, cols, ld_x: the input, as for the single calls;
+ *   tiling:  FP8BS_TILE_1x128 (needs cols % 128 == 0) or FP8BS_TILE_128x128
+ *            (needs rows % 128 == 0 and cols % 128 == 0);
+ *   q, ld_q: codes [rows, cols];
+ *   scale:   [rows, cols/128] (1x128) or [rows/128, cols/128] (128x128).
+ * n_jobs:  0 .. FP8BS_MAX_QUANT_JOBS.  Jobs with zero rows or columns are
+ *          skipped.  The outputs of different jobs must not overlap.
+ * Every job is validated before anything is enqueued; the error text names
+ * the failing job.
+ */
+#define FP8BS_MAX_QUANT_JOBS 8
+typedef struct fp8bs_quant_job {
+  const void* x;
+  int32_t x_dtype;
+  int32_t tiling;
+  int64_t rows;
+  int64_t cols;
+  int64_t ld_x;
+  uint8_t* q;
+  int64_t ld_q;
+  float* scale;
+} fp8bs_quant_job;
+
+fp8bs_status fp8_quant_batch(const fp8bs_quant_job* jobs, int32_t n_jobs, hipStream_t stream);
+
+/*
  * Both activation tilings of one tensor in a single pass over it: what
  * fp8_quant_act_1x128 writes with FP8BS_TILE_1x128 and with
  * FP8BS_TILE_128x1_T, from one read of x.  The backward pass needs both for

@@ -36,6 +36,20 @@ int main(void) {
   expect("grouped G", fp8_blockscaled_grouped_gemm(256, 256, 256, 0, (const int32_t*)fake, (const uint8_t*)fake, (const float*)fake,
                                                    (const uint8_t*)fake, (const float*)fake, (void*)fake, FP8BS_BF16,
                                                    0), FP8BS_ERR_INVALID_ARG);
+  {
+    fp8bs_quant_job jobs[2];
+    memset(jobs, 0, sizeof jobs);
+    jobs[0].x = fake; jobs[0].x_dtype = FP8BS_BF16; jobs[0].tiling = FP8BS_TILE_1x128;
+    jobs[0].rows = 4; jobs[0].cols = 256; jobs[0].ld_x = 256; jobs[0].q = (uint8_t*)fake; jobs[0].ld_q = 256;
+    jobs[0].scale = (float*)fake;
+    jobs[1] = jobs[0];
+    jobs[1].tiling = FP8BS_TILE_128x128; /* rows 4: not whole blocks */
+    expect("batch shape", fp8_quant_batch(jobs, 2, 0), FP8BS_ERR_SHAPE);
+    if (sizeof(fp8bs_quant_job) != 64) {
+      fprintf(stderr, "sizeof(fp8bs_quant_job) = %d\n", (int)sizeof(fp8bs_quant_job));
+      ++failures;
+    }
+  }
   expect("dual alignment", fp8_quant_act_dual((const char*)fake + 8, FP8BS_BF16, 128, 128, 128, (uint8_t*)fake, 128, (float*)fake,
                                               (uint8_t*)fake, 128, (float*)fake, 0), FP8BS_ERR_ALIGNMENT);
   expect("dequant tiling", fp8_dequant((const uint8_t*)fake, 4, 128, 128, (const float*)fake, FP8BS_TILE_128x1_T, (void*)fake,

@@ -21,6 +21,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = fb.header_functions()
     assert set(names) == {"fp8_quant_act_1x128", "fp8_quant_act_dual", "fp8_quant_w_128x128",
+                          "fp8_quant_batch",
                           "fp8_dequant", "fp8_quant_tensor", "fp8_blockscaled_gemm",
                           "fp8_blockscaled_gemm_fp8mma", "fp8_blockscaled_gemm_quant",
                           "fp8_blockscaled_grouped_gemm",
@@ -87,6 +88,35 @@ def test_quant_dual_validation(L):
     assert _dual(L, qt=A16 + 2) == ALIGN and _dual(L, ldqt=264) == ALIGN
     assert _dual(L, s=A16 + 1) == ALIGN and _dual(L, st=A4 + 2) == ALIGN
     assert _dual(L, ldx=(1 << 40) + 384) == INVALID
+
+
+def _job(x=A16, dt=0, tiling=0, rows=256, cols=384, ldx=384, q=A16, ldq=384, s=A16):
+    return fb.QuantJob(x, dt, tiling, rows, cols, ldx, q, ldq, s)
+
+
+def _batch(L, *jobs):
+    arr = (fb.QuantJob * max(1, len(jobs)))(*jobs)
+    return L.fp8_quant_batch(arr, len(jobs), None)
+
+
+def test_quant_batch_validation(L):
+    import ctypes
+    assert ctypes.sizeof(fb.QuantJob) == 64                       # the C struct's size
+    assert _batch(L) == OK                                         # no jobs
+    assert _batch(L, _job(rows=0), _job(cols=0, tiling=2)) == OK   # empty jobs are skipped
+    assert L.fp8_quant_batch(None, 1, None) == INVALID
+    assert L.fp8_quant_batch(None, -1, None) == INVALID
+    assert _batch(L, *[_job()] * 9) == INVALID                     # more than 8 jobs
+    assert _batch(L, _job(), _job(tiling=1)) == INVALID            # 128x1_T is not a batch tiling
+    assert "job 1" in fb.last_error()
+    assert _batch(L, _job(dt=5)) == INVALID
+    assert _batch(L, _job(cols=200, ldx=208, ldq=208)) == SHAPE
+    assert _batch(L, _job(tiling=2, rows=200)) == SHAPE            # 128x128 needs rows % 128
+    assert _batch(L, _job(), _job(q=NULL)) == INVALID and "job 1" in fb.last_error()
+    assert _batch(L, _job(x=A16 + 8)) == ALIGN and _batch(L, _job(s=A16 + 2)) == ALIGN
+    assert _batch(L, _job(ldx=256)) == INVALID                     # pitch < cols
+    assert _batch(L, _job(ldx=(1 << 40) + 384)) == INVALID
+    assert _batch(L, _job(rows=-1)) == INVALID
 
 
 def _deq(L, q=A16, rows=256, cols=384, ldq=384, s=A16, tiling=0, y=A16, ydt=1, ldy=384):

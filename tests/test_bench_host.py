@@ -69,10 +69,10 @@ def test_extra_oracle_samples_run():
     # The oracle leg of --extra-workloads on a reduced sample: every entry
     # names its sample and reports a positive throughput.
     b = _bench()
-    res = b.extra_cpu_baselines(shrink=16)
+    res = b.extra_cpu_baselines(shrink=8)
     assert set(res) == {"ffn_8192x18432x7168", "moe_grouped_32768x4096x7168_g16", "backward_dgrad_wgrad"}
     for v in res.values():
         assert v["kind"] == "oracle" and v["unit"] == "TFLOP/s"
         assert v["value"] > 0 and v["seconds"] > 0 and v["sample"]
         assert v["cores"]["quantize"] == 1 and v["cores"]["gemm"] >= 1
-    assert "X[64,7168]" in res["ffn_8192x18432x7168"]["sample"]
+    assert "X[128,7168]" in res["ffn_8192x18432x7168"]["sample"]
