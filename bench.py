@@ -43,8 +43,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "3f6cf08b0c5a964d01f11c467d2f8c9eefbd5444f25db659adcecae7418dfd3f",
-           "bytes_per_launch": 137155718,   # 120.38 MB read (FETCH_SIZE x 1.99948) + 16.78 MB written
+TRAFFIC = {"gemm_sha256": "12a78fb39703de2991e178668f463ff309e1a68b546a31f1118b724fdb1bcd8b",
+           "bytes_per_launch": 137174700,   # 120.40 MB read (FETCH_SIZE x 1.99946) + 16.78 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
