@@ -8,6 +8,12 @@ DeepSeek-V3 layer (hidden 7168), already resident in HBM; X, W and Y step
 through several buffer sets so that more than 1 GiB is cycled and the 256 MB
 Infinity Cache cannot serve repeated reads.
 
+Order of work: the per-kernel figures (linear workload, then the other
+workloads' shapes) come first, then W untimed steps and exactly K timed
+steps, then the CPU oracle.  The seconds of GPU work before the steps let the
+chip's clock settle: under sustained matrix work it goes through a transient
+of tens of milliseconds after an idle period.
+
 Prints one JSON line:
   value / ms_per_step  whole-step throughput: 2*M*N*K per step over the
                        measured step time (both quantizers included);
@@ -79,6 +85,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--launches", type=int, default=50,
                    help="back-to-back launches per kernel figure (at least 50)")
+    p.add_argument("--gemm-warmup", type=int, default=300,
+                   help="untimed GEMM launches before its back-to-back timing (the clock settles)")
     p.add_argument("--out", choices=["bf16", "f32"], default="bf16")
     p.add_argument("--rotate-mib", type=int, default=1100,
                    help="bytes of input/output buffers cycled through (defeats the MALL)")
@@ -327,7 +335,7 @@ def rand_bf16(torch, dev, shape, std=1.0, seed=0):
     return (torch.randn(shape, device=dev, generator=g) * std).to(torch.bfloat16)
 
 
-def linear_kernels(B, xs, ws, ys_dtype, qx_bytes, qw_bytes, flops):
+def linear_kernels(B, xs, ws, ys_dtype, qx_bytes, qw_bytes, flops, gemm_warmup):
     """Back-to-back figures of the step's kernels and the library's other
     kernels on the linear workload's shapes."""
     torch, dev, n = B.torch, B.dev, B.launches
@@ -346,12 +354,13 @@ def linear_kernels(B, xs, ws, ys_dtype, qx_bytes, qw_bytes, flops):
     qw_us = B.timed_us(lambda i: B.quant_w(ws[i % ns], b[i % ns], sb[i % ns]))
     both_us = B.timed_us(lambda i: (B.quant_act(xs[i % ns], a[i % ns], sa[i % ns]),
                                     B.quant_w(ws[i % ns], b[i % ns], sb[i % ns])))
-    # The GEMM draws enough power for the chip's clock to settle over a few
-    # milliseconds: 30 untimed launches (about 3 ms) come first, and the
-    # average is taken over at least 100 launches.
+    # Under sustained matrix work the chip's clock goes through a transient of
+    # tens of milliseconds before it settles: `gemm_warmup` untimed launches
+    # (default 300, about 33 ms) come first, and the average is taken over at
+    # least 100 launches.
     n_g = max(100, 2 * n)
     gemm_us = B.timed_us(lambda i: B.gemm(a[i % ns], sa[i % ns], b[i % ns], sb[i % ns], ys[i % ns]),
-                         n=n_g, warm=30)
+                         n=n_g, warm=gemm_warmup)
     out["quant_act_1x128"] = B.quant_rec(qx_bytes, qx_us, shape=[M, K], launches=n)
     out["quant_w_128x128"] = B.quant_rec(qw_bytes, qw_us, shape=[N, K], launches=n)
     out["quantize_two_launches"] = B.quant_rec(qx_bytes + qw_bytes, both_us, launches=n,
@@ -362,7 +371,7 @@ def linear_kernels(B, xs, ws, ys_dtype, qx_bytes, qw_bytes, flops):
                                        note="the step's quantization: X 1x128 and W 128x128 in one "
                                             "fp8_quant_batch launch")
     out["blockscaled_gemm"] = B.gemm_rec(flops, gemm_us, M=M, N=N, K=K, out="bf16" if ys_dtype == torch.bfloat16 else "f32",
-                                         mfma="bf16 (E4M3 widened exactly)", launches=n_g, warmup_launches=30)
+                                         mfma="bf16 (E4M3 widened exactly)", launches=n_g, warmup_launches=gemm_warmup)
     fp8_us = B.timed_us(lambda i: B.gemm(a[i % ns], sa[i % ns], b[i % ns], sb[i % ns], ys[i % ns],
                                          entry="fp8_blockscaled_gemm_fp8mma"), n=n_g, warm=30)
     out["blockscaled_gemm_fp8mma"] = B.gemm_rec(flops, fp8_us, mfma="fp8", launches=n_g,
@@ -597,6 +606,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # Per-kernel figures first: seconds of GPU work, so that the timed steps
+    # below run with the chip's clock settled.  (After an idle period the
+    # GEMM's clock goes through a transient of tens of milliseconds under
+    # sustained matrix work; see the kernel trace in profiles/.)
+    qx_bytes, qw_bytes, flops = algorithmic()
+    print(f"[bench] timing each kernel over at least {args.launches} back-to-back launches",
+          file=sys.stderr, flush=True)
+    kernels = linear_kernels(B, xs, ws, out_dtype, qx_bytes, qw_bytes, flops, args.gemm_warmup)
+    workloads = None
+    if not args.no_workloads:
+        print("[bench] timing the other workload shapes", file=sys.stderr, flush=True)
+        workloads = other_workloads(B)
+        torch.cuda.empty_cache()
+
     print(f"[bench] warmup {args.warmup} steps, {n_sets} buffer sets "
           f"({n_sets * set_bytes / 2**20:.0f} MiB cycled)", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -613,12 +636,9 @@ def main():
     end.record(B.stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
-    qx_bytes, qw_bytes, flops = algorithmic()
     value = flops / (ms_step * 1e-3) / 1e12
+    print(f"[bench] {ms_step * 1e3:.1f} us per step", file=sys.stderr, flush=True)
 
-    print(f"[bench] {ms_step * 1e3:.1f} us per step; timing each kernel over {args.launches} "
-          "back-to-back launches", file=sys.stderr, flush=True)
-    kernels = linear_kernels(B, xs, ws, out_dtype, qx_bytes, qw_bytes, flops)
     g = kernels["blockscaled_gemm"]
     gemm_src = os.path.join(ROOT, "fp8_block_scaled_05_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(gemm_src, "rb").read()).hexdigest()
@@ -650,9 +670,8 @@ def main():
                      "note": "the exact GEMM runs on the bf16 matrix instructions (2.5 PFLOP/s peak)"},
         "kernels": kernels,
     }
-    if not args.no_workloads:
-        print("[bench] timing the other workload shapes", file=sys.stderr, flush=True)
-        result["workloads"] = other_workloads(B)
+    if workloads is not None:
+        result["workloads"] = workloads
     if not args.no_cpu_baseline:
         print(f"[bench] timing the CPU oracle on {args.cpu_rows} rows", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(xbits, wbits, args.cpu_rows)
