@@ -129,13 +129,9 @@ struct GemmArgs {
   int32_t G;
 };
 
-// kStages: LDS stages in the K-block ring (2 or 3).  kMinWaves: waves per
-// SIMD the register budget must allow (2 keeps a wave at 256 registers, so
-// that two 4-wave workgroups share a CU).
-template <int BM_, int BN_, int WM_, int WN_, int kStages_ = 3, int kMinWaves_ = 1>
+template <int BM_, int BN_, int WM_, int WN_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr int kStages = kStages_, kMinWaves = kMinWaves_;
   static constexpr int kWaves = WM * WN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
@@ -254,13 +250,10 @@ __device__ __forceinline__ w8 widen8(uint32_t w0, uint32_t w1) {
 
 // ---------------------------------------------------------------------------
 template <class C, bool kWiden, bool kRowScale, int kOut, bool kGrouped>
-__global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const GemmArgs args) {
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs args) {
   using St = Stage<C::BM, C::BN>;
   using Sg = ScaleGroup<C::BM, C::BN, kRowScale>;
-  struct NoStage { uint8_t unused[16]; };
-  using St3 = typename std::conditional<C::kStages == 3, St, NoStage>::type;
-  __shared__ St st0, st1;
-  __shared__ St3 st2;
+  __shared__ St st0, st1, st2;
   __shared__ Sg sg[2];
   constexpr int SM = C::SM, SN = C::SN, NW = C::kWaves;
 
@@ -384,11 +377,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   // instructions rather than in one run after the barrier, where both waves
   // of a SIMD would reach them together and leave the matrix core idle.
   // (Finishing before the slice after the barrier keeps the kernel within
-  // the register budget without spills.)  Which blocks are
-  // deferred is fixed per unrolled step (see the main loops).  Otherwise
-  // (FP8 path, per-row B scales) p[0] holds every block and is promoted at
-  // the end of its step.  Either way each accumulator receives the same FMAs
-  // in the same order.
+  // the register budget without spills.)  Which blocks are deferred is
+  // fixed per unrolled step (see the main loops).  Otherwise (FP8 path,
+  // per-row B scales) p[0] holds every block and is promoted at the end of
+  // its step.  (Deferring per-row promotions the same way measured no
+  // faster: that path is bound by its vector instructions, the conversions
+  // plus a scale product per accumulator, not by their placement.)  Either
+  // way each accumulator receives the same FMAs in the same order.
   constexpr bool kLag = kWiden && !kRowScale;
   v16f p[2][SM][SN];
   float cl[SM];   // kLag: sa * sb of the pending block
@@ -404,6 +399,20 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     constexpr int par = decltype(par_c)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[par][i][j][r], c, acc[i][j][r]);
+  };
+  // Per-row B scales: column slab j of block kbv from p[par], with A scales
+  // ca.  The slab's 16 accumulators per lane are 16 columns, each with its
+  // own B scale (read from the scale group) and product sa * sb.
+  auto promote_row = [&](auto par_c, int j, int kbv, const float (&ca)[SM]) {
+    constexpr int par = decltype(par_c)::value;
+    const Sg& g = sg[(kbv >> 2) & 1];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float sbn = g.sb[wn * C::TN + 32 * j + 8 * (r >> 2) + 4 * hk + (r & 3)][kbv & 3];
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        acc[i][j][r] = __builtin_fmaf(p[par][i][j][r], ca[i] * sbn, acc[i][j][r]);
+    }
   };
   // kLag: the pending block's subtiles s = i * SN + j with s / 2 == q.  The
   // empty asm makes the updated accumulators live at this point, so the
@@ -493,15 +502,13 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
   // read of stage s is issued before the barrier, which is what lets the
   // next step refill it.  The scales are read after it: their group buffer
   // is refilled only two steps later.
-  // after_barrier runs right after the block's barrier (the 2-stage ring
-  // issues its loads there, into the stage just released).
   // The lag arguments are std::integral_constant (p[] is indexed
   // statically) and matter only with kLag: par_c, the buffer this block
   // accumulates into; in_c, promote the pending block of the other buffer
   // during this one; keep_c, leave this block pending (else it is promoted
   // at the end of the step).
   auto step = [&](auto par_c, auto in_c, auto keep_c, const St& s, const St& nxt, int kb, float sbv,
-                  int mode, auto&& after_barrier) {
+                  int mode) {
     using Par = std::integral_constant<int, kLag ? decltype(par_c)::value : 0>;
     constexpr bool kIn = kLag && decltype(in_c)::value;
     constexpr bool kKeep = kLag && decltype(keep_c)::value;
@@ -524,7 +531,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     }
     if (mode == 1) wait_and_barrier<kLoadsPerStage>();
     else if (mode == 2) wait_and_barrier<0>();
-    after_barrier();
     if (mode != 0) {
       if constexpr (kWiden) read_slice(nxt, 0, 0);
       else read_slice8(nxt, 0, 0);
@@ -552,54 +558,28 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
       for (int i = 0; i < SM; ++i) {
         const float c = ca[i] * sbv;
 #pragma unroll
-        for (int j = 0; j < SN; ++j) promote(Par{}, i, j, c);
+        for (int j = 0; j < SN; ++j) {
+          promote(Par{}, i, j, c);
+          keep_in_vgprs(acc[i][j]);
+        }
       }
     } else {
+      // Per-row B scales, one column slab at a time; the empty asm keeps the
+      // compiler from sinking these FMAs into the next step, which would hold
+      // the slab's B scales across it and spill.
 #pragma unroll
-      for (int j = 0; j < SN; ++j)
+      for (int j = 0; j < SN; ++j) {
+        promote_row(Par{}, j, kb, ca);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float sbn = scl.sb[wn * C::TN + 32 * j + 8 * (r >> 2) + 4 * hk + (r & 3)][kb & 3];
-#pragma unroll
-          for (int i = 0; i < SM; ++i)
-            acc[i][j][r] = __builtin_fmaf(p[0][i][j][r], ca[i] * sbn, acc[i][j][r]);
-        }
+        for (int i = 0; i < SM; ++i) keep_in_vgprs(acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
   // A grouped wave with no rows of its expert (see below) skips the matrix
   // work but still takes every barrier, the epilogue's included.
   bool idle = false;
-  if constexpr (C::kStages == 2) {
-    // Two-stage ring: block kb is in stage kb % 2.  The barrier of step kb
-    // (before its last slice) waits for block kb + 1 and, since every read of
-    // stage kb % 2 precedes it, releases that stage: block kb + 2 is loaded
-    // into it right after the barrier, one step ahead of its use.  Scale
-    // group g + 1 is loaded after the barrier of step 4 g + 1; its buffer
-    // held group g - 1, last read by step 4 g - 1.
-    load_scales(0);
-    load_stage(st0, 0);
-    wait_and_barrier<0>();
-    if (KB > 1) load_stage(st1, 1);
-    if constexpr (kWiden) read_slice(st0, 0, 0);
-    else read_slice8(st0, 0, 0);
-#define FP8BS_STEP2(PAR, CUR, NXT, KBV)                                         \
-    if ((KBV) < KB) {                                                           \
-      const int kb_ = (KBV);                                                    \
-      const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                        \
-      step(std::integral_constant<int, (PAR)>{}, std::true_type{},              \
-           std::true_type{}, CUR, NXT, kb_, sbv_,                               \
-           kb_ + 1 < KB ? 2 : 0, [&] {                                          \
-        if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);        \
-        if (kb_ + 2 < KB) load_stage(CUR, kb_ + 2);                             \
-      });                                                                       \
-    }
-    for (int kb = 0; kb < KB; kb += 2) {
-      FP8BS_STEP2(0, st0, st1, kb)
-      FP8BS_STEP2(1, st1, st0, kb + 1)
-    }
-#undef FP8BS_STEP2
-  } else {
   if constexpr (kGrouped) {
     // A wave whose TM-row slab lies entirely past its group's last row (in
     // an expert's tail tile) has nothing to multiply.  It issues its share
@@ -655,7 +635,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     if ((kb_ & 3) == 1 && kb_ + 3 < KB) load_scales((kb_ >> 2) + 1);      \
     load_stage(FUT, kb_ + 2);                                             \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
-    step(KIND##_PAR{}, KIND##_IN{}, KIND##_KEEP{}, CUR, NXT, kb_, sbv_, 1, [] {}); \
+    step(KIND##_PAR{}, KIND##_IN{}, KIND##_KEEP{}, CUR, NXT, kb_, sbv_, 1);  \
   }
 #define FP8BS_STEP_TAIL(KIND, CUR, NXT, FUT, KBV)                          \
   if ((KBV) < KB) {                                                       \
@@ -664,7 +644,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
     if (kb_ + 2 < KB) load_stage(FUT, kb_ + 2);                           \
     const float sbv_ = kRowScale ? 1.0f : sb_blk[kb_];                    \
     step(KIND##_PAR{}, KIND##_IN{}, KIND##_KEEP{}, CUR, NXT, kb_, sbv_,   \
-         kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2), [] {});               \
+         kb_ + 1 >= KB ? 0 : (kb_ + 2 < KB ? 1 : 2));                      \
   }
   // With kLag, blocks 3 j, 3 j + 1, 3 j + 2 are steps of kinds A, B, C:
   // A accumulates into p[0] and stays pending; B promotes it while
@@ -695,13 +675,11 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 #undef FP8BS_STEP_FULL
 #undef FP8BS_STEP_TAIL
   }  // !idle
-  }
 
-  // kLag: the last block, K block KB - 1, may still be pending: in
-  // p[(KB - 1) & 1] on the two-stage ring; on the three-stage ring in p[0]
+  // kLag: the last block, K block KB - 1, may still be pending: in p[0]
   // after an A step and in p[1] after a B step.
   if constexpr (kLag) {
-    const int last = idle ? -1 : (C::kStages == 2 ? ((KB - 1) & 1) : ((KB - 1) % 3));
+    const int last = idle ? -1 : (KB - 1) % 3;
 #pragma unroll
     for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -839,11 +817,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinWaves) void gemm_kernel(const G
 // ---------------------------------------------------------------------------
 using CfgLarge = TileCfg<256, 128, 4, 2>;   // 256 x 128 tile, 8 waves of 64 x 64
 using CfgSmall = TileCfg<128, 128, 2, 2>;   // 128 x 128 tile, 4 waves of 64 x 64
-// 128 x 128 tile, 4 waves of 64 x 64, two LDS stages: two workgroups share a
-// CU and keep their own barriers.  Used for per-row B scales, whose
-// promotion needs a scale product per accumulator: the 256 x 128 tile
-// spills there (~40 registers) and this one does not.
-using CfgPair = TileCfg<128, 128, 2, 2, 2, 2>;
 
 // Launches the kernel variant for one tile configuration; `out` is an
 // OutKind.  Only the variants the entry points can reach are instantiated:
@@ -915,9 +888,9 @@ fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const u
   args.G = 1;
   const bool row = b_kind == FP8BS_BSCALE_ROW;
   const int64_t tiles_large = ((M + 255) / 256) * ((N + 127) / 128);
-  // Per-row B scales on a large output: the paired 128 x 128 tile; block-128
-  // B scales: the 256 x 128 tile; small outputs: the 128 x 128 tile.
-  const int bm = tiles_large >= kNumCU && !row ? 256 : 128;
+  // The 256 x 128 tile when it gives at least one workgroup per CU, else
+  // the 128 x 128 tile.
+  const int bm = tiles_large >= kNumCU ? 256 : 128;
   args.tiles_m = int32_t((M + bm - 1) / bm);
   args.tiles_n = int32_t((N + 127) / 128);
   const int64_t n_wg = int64_t(args.tiles_m) * args.tiles_n;
@@ -925,7 +898,7 @@ fp8bs_status dense_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const u
   begin_launch();
 #define FP8BS_DENSE(W)                                                                         \
   if (tiles_large >= kNumCU) {                                                                 \
-    if (row) launch_cfg<CfgPair, W, true, false>(args, out, uint32_t(n_wg), stream);           \
+    if (row) launch_cfg<CfgLarge, W, true, false>(args, out, uint32_t(n_wg), stream);           \
     else launch_cfg<CfgLarge, W, false, false>(args, out, uint32_t(n_wg), stream);             \
   } else {                                                                                     \
     if (row) launch_cfg<CfgSmall, W, true, false>(args, out, uint32_t(n_wg), stream);          \

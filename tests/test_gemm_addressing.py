@@ -15,7 +15,7 @@ import itertools
 import pytest
 
 # (BM, BN, waves) of the three tile configurations.
-CONFIGS = {"large": (256, 128, 8), "small": (128, 128, 4), "pair": (128, 128, 4)}
+CONFIGS = {"large": (256, 128, 8), "small": (128, 128, 4)}
 
 
 def swz(row):

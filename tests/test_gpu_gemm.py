@@ -163,8 +163,8 @@ def _int_codes(rng, shape):
 @pytest.mark.parametrize("m,n,k,kind,out", [(256, 256, 7168, "block128", "f32"),
                                             (300, 384, 1024, "row", "f32"),
                                             (129, 128, 128, "block128", "f32"),
-                                            (4096, 2048, 1024, "row", "f32"),   # paired 128x128 tiles
-                                            (4000, 2064, 640, "row", "f32")])   # paired, ragged M and N
+                                            (4096, 2048, 1024, "row", "f32"),   # 256 x 128 tiles
+                                            (4000, 2064, 640, "row", "f32")])   # 256 x 128, ragged M and N
 def test_integer_exact_is_bit_exact(m, n, k, kind, out):
     rng = np.random.default_rng([20, m, n, k])
     a = _int_codes(rng, (m, k))
@@ -179,23 +179,25 @@ def test_integer_exact_is_bit_exact(m, n, k, kind, out):
     assert np.array_equal(_y_host(y), ref)
 
 
+@pytest.mark.parametrize("kind", ["block128", "row"])
 @pytest.mark.parametrize("k", [128, 256, 384, 512, 640, 768, 896])
-def test_large_tile_integer_exact_every_tail(k):
+def test_large_tile_integer_exact_every_tail(k, kind):
     """4096 x 2048 runs the 256 x 128 tile.  Its main loop takes three K
-    blocks at a time and may leave the last block's promotion pending, so
-    K / 128 = 1 .. 7 covers every tail and every pending state; with
-    integer-valued codes and power-of-two scales the result is exact."""
+    blocks at a time and, with block-128 B scales, may leave the last
+    block's promotion pending, so K / 128 = 1 .. 7 covers every tail and
+    every pending state; with integer-valued codes and power-of-two scales
+    the result is exact."""
     m, n = 4096, 2048
     rng = np.random.default_rng([25, k])
     a = _int_codes(rng, (m, k))
     b = _int_codes(rng, (n, k))
     sa = rng.choice(np.float32([1.0, 2.0]), size=(m, k // 128))
-    sb = rng.choice(np.float32([0.5, 1.0]), size=(n // 128, k // 128))
-    banner(f"gemm integer-exact large tile {m}x{n}x{k}")
-    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), "block128", torch.float32)
+    sb = rng.choice(np.float32([0.5, 1.0]), size=(n // 128 if kind == "block128" else n, k // 128))
+    banner(f"gemm integer-exact large tile {m}x{n}x{k} {kind}")
+    y = fb.fp8_blockscaled_gemm(_dev(a), _dev(sa), _dev(b), _dev(sb), kind, torch.float32)
     torch.cuda.synchronize()
     rows = synth.sample_rows(m, 256, seed=k, must=[0, m - 1])
-    ref, _ = oracle.blockscaled_gemm_ref(a[rows], sa[rows], b, sb)
+    ref, _ = oracle.blockscaled_gemm_ref(a[rows], sa[rows], b, sb, kind)
     assert np.array_equal(_y_host(y)[rows], ref)
 
 
