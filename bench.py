@@ -49,8 +49,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "12a78fb39703de2991e178668f463ff309e1a68b546a31f1118b724fdb1bcd8b",
-           "bytes_per_launch": 137174700,   # 120.40 MB read (FETCH_SIZE x 1.99946) + 16.78 MB written
+TRAFFIC = {"gemm_sha256": "dac456761549eb215ad1fa1308cb8dbd33de02f253aa06c637085b5ebb8f5752",
+           "bytes_per_launch": 137170971,   # 120.39 MB read (FETCH_SIZE x 1.99941) + 16.78 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
@@ -449,7 +449,12 @@ def other_workloads(B):
     torch, dev = B.torch, B.dev
     bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
     n_gemm = max(20, B.launches // 2)
-    w_gemm = 10                         # untimed launches first: the clock settles under load
+
+    def w_gemm(flops):
+        # Untimed launches first, about 30 ms of matrix work (at least 10):
+        # the chip's clock goes through a transient of tens of milliseconds
+        # under sustained matrix work before it settles.
+        return max(10, -(-30000 * 12 // (flops // 10**8)))
     res = {}
 
     def quantize_pair(x, w, w_t=False):
@@ -475,14 +480,15 @@ def other_workloads(B):
     a, sa, b, sb, _ = quantize_pair(x, w)
     y = torch.empty((m, n), dtype=bf, device=dev)
     sets = rotate([a, sa, b, sb, y])
-    us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)]), n=n_gemm, warm=w_gemm)
+    us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)]), n=n_gemm, warm=w_gemm(2 * m * n * k))
     qa = [torch.empty((m, k), dtype=u8, device=dev), torch.empty((m, k // 128), dtype=f32, device=dev)]
     qb = [torch.empty((n, k), dtype=u8, device=dev), torch.empty((n // 128, k // 128), dtype=f32, device=dev)]
     x2, w2 = x.clone(), w.clone()
     qx_us = B.timed_us(lambda i: B.quant_act((x, x2)[i % 2], *qa))
     qw_us = B.timed_us(lambda i: B.quant_w((w, w2)[i % 2], *qb))
     res["ffn_8192x18432x7168"] = {
-        "gemm": B.gemm_rec(2 * m * n * k, us, M=m, N=n, K=k, out="bf16", launches=n_gemm),
+        "gemm": B.gemm_rec(2 * m * n * k, us, M=m, N=n, K=k, out="bf16", launches=n_gemm,
+                           warmup_launches=w_gemm(2 * m * n * k)),
         "quant_x_1x128": B.quant_rec(quant_bytes(m, k, "1x128"), qx_us, shape=[m, k], launches=B.launches),
         "quant_w_128x128": B.quant_rec(quant_bytes(n, k, "128x128"), qw_us, shape=[n, k], launches=B.launches)}
     del x, w, x2, w2, a, sa, b, sb, y, sets, qa, qb
@@ -499,12 +505,13 @@ def other_workloads(B):
     b, sb = b.view(g, n, k), sb.view(g, n // 128, k // 128)
     y = torch.empty((m, n), dtype=bf, device=dev)
     sets = rotate([a, sa, b, sb, y])
-    us = B.timed_us(lambda i: B.grouped(off, *sets[i % len(sets)]), n=n_gemm, warm=w_gemm)
+    us = B.timed_us(lambda i: B.grouped(off, *sets[i % len(sets)]), n=n_gemm, warm=w_gemm(2 * m * n * k))
     qx_us = B.timed_us(lambda i: B.quant_act(x, a, sa))
     qw_us = B.timed_us(lambda i: B.quant_w(w, b.view(g * n, k), sb.view(g * n // 128, k // 128)))
     res["moe_grouped_32768x4096x7168_g16"] = {
         "counts": counts.tolist(),
-        "gemm": B.gemm_rec(2 * m * n * k, us, M_total=m, N=n, K=k, G=g, out="bf16", launches=n_gemm),
+        "gemm": B.gemm_rec(2 * m * n * k, us, M_total=m, N=n, K=k, G=g, out="bf16", launches=n_gemm,
+                           warmup_launches=w_gemm(2 * m * n * k)),
         "quant_x_1x128": B.quant_rec(quant_bytes(m, k, "1x128"), qx_us, shape=[m, k], launches=B.launches),
         "quant_w_128x128": B.quant_rec(quant_bytes(g * n, k, "128x128"), qw_us, shape=[g * n, k],
                                        launches=B.launches, note="the 16 expert weights as one call")}
@@ -520,7 +527,7 @@ def other_workloads(B):
     wst = ws.t().contiguous()
     y = torch.empty((t, h), dtype=bf, device=dev)
     sets = rotate([g_, sg_, wt, wst, y])
-    dgrad_us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)]), n=n_gemm, warm=w_gemm)
+    dgrad_us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)]), n=n_gemm, warm=w_gemm(2 * t * h * f))
     del sets, y
     xt = torch.empty((h, t), dtype=u8, device=dev)
     sxt = torch.empty((h, t // 128), dtype=f32, device=dev)
@@ -532,7 +539,7 @@ def other_workloads(B):
     B.quant_dual(dy, gq, sgq, gt, sgt)
     dw = torch.empty((h, f), dtype=f32, device=dev)
     sets = rotate([xt, sxt, gt, sgt, dw])
-    wgrad_us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)], kind=1), n=n_gemm, warm=w_gemm)
+    wgrad_us = B.timed_us(lambda i: B.gemm(*sets[i % len(sets)], kind=1), n=n_gemm, warm=w_gemm(2 * t * h * f))
     del sets
     dys = [dy] + [dy.clone() for _ in range(B.n_sets(t * f * 2 * 3, cap=16) - 1)]
     xs = [x, x.clone()]
@@ -542,9 +549,11 @@ def other_workloads(B):
     wt_us = B.timed_us(lambda i: B.quant_w(ws_[i % len(ws_)], wq, ws, wt))
     res["backward_8192x7168x2048"] = {
         "dgrad_gemm": B.gemm_rec(2 * t * h * f, dgrad_us, M=t, N=h, K=f, out="bf16",
-                                 b="W^T codes from the 128x128 quantizer's transposed copy", launches=n_gemm),
+                                 b="W^T codes from the 128x128 quantizer's transposed copy", launches=n_gemm,
+                                 warmup_launches=w_gemm(2 * t * h * f)),
         "wgrad_gemm": B.gemm_rec(2 * h * f * t, wgrad_us, M=h, N=f, K=t, out="f32", b_scales="row",
-                                 operands="X^T and dY^T, 128x1 tiles along the tokens", launches=n_gemm),
+                                 operands="X^T and dY^T, 128x1 tiles along the tokens", launches=n_gemm,
+                                 warmup_launches=w_gemm(2 * t * h * f)),
         "quant_dy_dual": B.quant_rec(quant_bytes(t, f, "dual"), dual_us, shape=[t, f], launches=B.launches,
                                      note="dY 1x128 (dgrad) and 128x1 transposed (wgrad) from one read"),
         "quant_x_128x1_t": B.quant_rec(quant_bytes(t, h, "128x1_t"), xt_us, shape=[t, h], launches=B.launches),
