@@ -104,10 +104,14 @@ __global__ __launch_bounds__(64) void fill_kernel(float* p, float v) {
 // Each thread takes kU chunks per pass of its grid-stride loop (chunks
 // kTT u + t of a kTT kU block), all loads issued before their use.
 constexpr int kTU = 4;
-// One workgroup of 1024 threads per CU: at most 256 amax atomics per call,
-// and 16 waves x 4 chunks of loads in flight per CU.
+// Two workgroups of 1024 threads per CU (at most 64 registers per thread):
+// at most 512 amax atomics per call, and 32 waves x 4 chunks of loads in
+// flight per CU.  The grid is balanced so that every pass of the
+// grid-stride loop is full but the last by less than one workgroup's share
+// (a grid of 512 over 3.5 passes' worth of chunks would leave the last pass
+// half idle).
 constexpr int kTT = 1024;
-constexpr int kTGrid = 256;
+constexpr int kTGrid = 512;
 
 template <bool kBf16>
 __device__ __forceinline__ const char* chunk_ptr(const void* x, int64_t ld_x, FastDiv per_row, uint32_t c,
@@ -144,8 +148,12 @@ __global__ __launch_bounds__(kTT) void tensor_amax_kernel(const void* __restrict
 // amax is accumulated into *amax_out; otherwise from *src (the amax of x).
 // Quotients: with current scaling |x / s| <= 448 and Markstein's correction
 // of x * fl32(1/s) (see div_bf16_by_scale) is the correctly rounded quotient
-// wherever the code is not zero; a stale delayed scale can make x / s
-// overflow, so the delayed kernel divides (IEEE) and saturates.
+// wherever the code is not zero.  A stale delayed scale can make x / s
+// exceed the format's range, even overflow float32, where the correction
+// breaks down (x * r = inf gives NaN); there the code saturates whatever
+// the exact quotient is, so when |x * r| > 2 * max (then |x / s| > max too)
+// the kernel takes +-max directly and the correction everywhere else.  The
+// codes equal those of the IEEE quotient clamped to +-max.
 template <bool kBf16, bool kE5M2, bool kDelayed>
 __global__ __launch_bounds__(kTT) void tensor_quant_kernel(const void* __restrict__ x, int64_t ld_x,
                                                            uint32_t n_chunks, FastDiv per_row,
@@ -185,7 +193,9 @@ __global__ __launch_bounds__(kTT) void tensor_quant_kernel(const void* __restric
       for (int i = 0; i < 8; ++i) {
         if constexpr (kDelayed) {
           m = fmaxf(m, fabsf(v[u][i]));
-          w[i] = fminf(fmaxf(v[u][i] / s, -kMax), kMax);
+          const float q0 = v[u][i] * r;
+          w[i] = fabsf(q0) > 2.0f * kMax ? __builtin_copysignf(kMax, v[u][i])
+                                         : fminf(fmaxf(div_bf16_by_scale(v[u][i], s, r), -kMax), kMax);
         } else {
           w[i] = fminf(fmaxf(div_bf16_by_scale(v[u][i], s, r), -kMax), kMax);
         }
@@ -253,7 +263,9 @@ extern "C" fp8bs_status fp8_quant_tensor(const void* x, int32_t x_dtype, int64_t
   const int64_t n_chunks = rows * per_row;
   if (n_chunks > 0xf0000000LL) return fail(FP8BS_ERR_INVALID_ARG, "%s: more than 2^32 chunks", fn);
   const FastDiv div(static_cast<uint32_t>(per_row));
-  const uint32_t grid = static_cast<uint32_t>(std::min<int64_t>((n_chunks + kTT * kTU - 1) / (kTT * kTU), kTGrid));
+  const int64_t per_pass = int64_t(kTGrid) * kTT * kTU;
+  const int64_t passes = (n_chunks + per_pass - 1) / per_pass;
+  const uint32_t grid = static_cast<uint32_t>((n_chunks + passes * kTT * kTU - 1) / (passes * kTT * kTU));
   const double widen = 1.0 + margin;
   const bool bf16 = x_dtype == FP8BS_BF16, e5 = format == FP8BS_FMT_E5M2;
 

@@ -117,3 +117,26 @@ def test_e5m2_every_bf16_value():
     q, s, _ = _run(dev_bf16(synth.f32_to_bf16_bits(x)), fmt="e5m2")
     assert s[0] == 1.0
     assert_codes_equal(q, oracle.e5m2_encode(x), "codes")
+
+
+@pytest.mark.parametrize("fmt,stale", [("e4m3", 1e-3), ("e4m3", 3.0), ("e5m2", 0.5)])
+def test_delayed_scaling_every_bf16_value_stale_scale(fmt, stale):
+    """A stale delayed scale against every finite bf16 value: the quotients
+    x / s run from far below the smallest code through the format's range to
+    float32 overflow (1e-3 / 448 makes every |x| above ~7.5e32 overflow), so
+    the saturating, the exact and the flushed-to-zero codes are all checked
+    against the oracle's float32 quotient and encoder."""
+    v = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    v = v[np.isfinite(v)]
+    v = np.concatenate([v, np.zeros(-len(v) % 64, np.float32)])
+    x = v.reshape(-1, 64)
+    bits = synth.f32_to_bf16_bits(x)
+    hist = np.float32([stale, stale / 2])
+    hd = dev_f32(hist)
+    banner(f"per-tensor delayed {fmt}, stale history {stale}, every bf16 value ({v.size})")
+    q, s, a = _run(dev_bf16(bits), fmt=fmt, history=hd)
+    want_q, want_s, want_a, want_h = oracle.quant_tensor_delayed(f32(bits), hist, fmt)
+    assert_scales_equal(s, np.float32([want_s]), "scale")
+    assert_scales_equal(a, np.float32([want_a]), "amax")
+    assert_codes_equal(q, want_q, "codes")
+    assert_scales_equal(host(hd), want_h, "history")
