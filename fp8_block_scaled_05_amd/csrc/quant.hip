@@ -316,10 +316,12 @@ __device__ __forceinline__ void unpack8(const u32x4 (&d)[kBf16 ? 1 : 2], float (
 }
 
 // Workgroup g handles blocks g, g + gridDim.x, ... (block b = row block
-// b / col_blocks, column block b % col_blocks), reading block i + 1 into
-// registers while block i is reduced, encoded and stored, so that loads and
-// stores of different blocks overlap.
-template <bool kBf16, bool kTrans, int kThreads, bool kNT>
+// b / col_blocks, column block b % col_blocks).  kPersist (grids smaller
+// than the block count): it reads block i + 1 into registers while block i
+// is reduced, encoded and stored, so that loads and stores of different
+// blocks overlap.  Otherwise each workgroup takes one block and holds no
+// second buffer, which leaves registers for more workgroups per CU.
+template <bool kBf16, bool kTrans, int kThreads, bool kNT, bool kPersist>
 __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __restrict__ w, int64_t ld_w,
                                                                  int64_t rows, int64_t cols,
                                                                  uint8_t* __restrict__ q, int64_t ld_q,
@@ -345,9 +347,11 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
     const uint32_t bi = blk / col_blocks, bj = blk % col_blocks;
     const int64_t r0 = int64_t(bi) * 128, c0 = int64_t(bj) * 128;
     const uint32_t nb = blk + gridDim.x;
-    if (nb < n_blocks)
-      load_rows<kBf16, kRows, kRowStep>(nxt, w, ld_w, int64_t(nb / col_blocks) * 128,
-                                        int64_t(nb % col_blocks) * 128, rbase, cc);
+    if constexpr (kPersist) {
+      if (nb < n_blocks)
+        load_rows<kBf16, kRows, kRowStep>(nxt, w, ld_w, int64_t(nb / col_blocks) * 128,
+                                          int64_t(nb % col_blocks) * 128, rbase, cc);
+    }
 
     float v[kRows][8];
 #pragma unroll
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
       }
       __syncthreads();   // ct is rewritten by the next block
     }
-    cur = nxt;
+    if constexpr (kPersist) cur = nxt; else break;
   }
 }
 
@@ -421,12 +425,14 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
 //    maxima into scales; every thread encodes its values with its columns'
 //    scales into an LDS byte tile, and 8x8 byte transposes turn that into
 //    whole 128-byte rows of q_t.
-// The next block's input is loaded into registers while the current one is
-// processed.  Three barriers per block; the LDS buffers written after each
-// one were last read before the previous one.
+// With kPersist (a grid smaller than the block count), the next block's
+// input is loaded into registers while the current one is processed;
+// otherwise each workgroup takes one block and holds no second buffer.
+// Three barriers per block; the LDS buffers written after each one were last
+// read before the previous one.
 // kRowOut false: only the 128x1 output (the 128x1_T tiling of
 // fp8_quant_act_1x128 when cols is a multiple of 128).
-template <bool kBf16, int kThreads, bool kRowOut, bool kNT>
+template <bool kBf16, int kThreads, bool kRowOut, bool kNT, bool kPersist>
 __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __restrict__ x, int64_t ld_x,
                                                               int64_t rows, int64_t cols,
                                                               uint8_t* __restrict__ q, int64_t ld_q,
@@ -459,9 +465,11 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
     const uint32_t bi = blk / col_blocks, bj = blk % col_blocks;
     const int64_t r0 = int64_t(bi) * 128, c0 = int64_t(bj) * 128;
     const uint32_t nb = blk + gridDim.x;
-    if (nb < n_blocks)
-      load_rows<kBf16, kRows, kRowStep>(nxt, x, ld_x, int64_t(nb / col_blocks) * 128,
-                                        int64_t(nb % col_blocks) * 128, rbase, cc);
+    if constexpr (kPersist) {
+      if (nb < n_blocks)
+        load_rows<kBf16, kRows, kRowStep>(nxt, x, ld_x, int64_t(nb / col_blocks) * 128,
+                                          int64_t(nb % col_blocks) * 128, rbase, cc);
+    }
     float v[kRows][8];
 #pragma unroll
     for (int p = 0; p < kRows; ++p) unpack8<kBf16>(cur.d[p], v[p]);
@@ -546,7 +554,7 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
       for (int jj = 0; jj < 8; ++jj)
         store_codes8<kNT>(q_t + (c0 + 8 * b + jj) * ld_qt + r0 + 8 * a, make_uint2(col_lo[jj], col_hi[jj]));
     }
-    cur = nxt;
+    if constexpr (kPersist) cur = nxt; else break;
   }
 }
 
@@ -755,11 +763,13 @@ extern "C" fp8bs_status fp8_quant_act_1x128(const void* x, int32_t x_dtype, int6
     const dim3 grid(static_cast<uint32_t>((n_blocks + per_wg - 1) / per_wg));
     constexpr int kT = FP8BS_DUAL_THREADS;
     const bool cached = rows * cols <= int64_t(FP8BS_CACHED_CODE_BYTES);
-#define FP8BS_TL(B, NT) hipLaunchKernelGGL((quant_dual_kernel<B, kT, false, NT>), grid, dim3(kT), 0, stream, x, ld_x, \
-                                           rows, cols, nullptr, int64_t(0), nullptr, q, ld_q, scale)
+#define FP8BS_TLP(B, NT, P) hipLaunchKernelGGL((quant_dual_kernel<B, kT, false, NT, P>), grid, dim3(kT), 0, stream, \
+                                               x, ld_x, rows, cols, nullptr, int64_t(0), nullptr, q, ld_q, scale)
+#define FP8BS_TL(B, NT) do { if (per_wg > 1) FP8BS_TLP(B, NT, true); else FP8BS_TLP(B, NT, false); } while (0)
     if (bf16) { if (cached) FP8BS_TL(true, false); else FP8BS_TL(true, true); }
     else { if (cached) FP8BS_TL(false, false); else FP8BS_TL(false, true); }
 #undef FP8BS_TL
+#undef FP8BS_TLP
   } else {
     if ((cols + 63) / 64 > 0x7fffffff || rows / 128 > 65535)
       return fail(FP8BS_ERR_INVALID_ARG, "%s: too many tiles for the launch grid", fn);
@@ -803,8 +813,9 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
   // with ordinary stores, larger outputs stream past the caches.
   const bool cached = rows * cols * (q_t ? 2 : 1) <= int64_t(FP8BS_CACHED_CODE_BYTES);
   begin_launch();
-#define FP8BS_WL(B, T, NT) hipLaunchKernelGGL((quant_128x128_kernel<B, T, kT, NT>), grid, dim3(kT), 0, stream, \
-                                              w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt)
+#define FP8BS_WLP(B, T, NT, P) hipLaunchKernelGGL((quant_128x128_kernel<B, T, kT, NT, P>), grid, dim3(kT), 0, \
+                                                  stream, w, ld_w, rows, cols, q, ld_q, scale, q_t, ld_qt)
+#define FP8BS_WL(B, T, NT) do { if (per_wg > 1) FP8BS_WLP(B, T, NT, true); else FP8BS_WLP(B, T, NT, false); } while (0)
 #define FP8BS_WL2(B, T) if (cached) FP8BS_WL(B, T, false); else FP8BS_WL(B, T, true);
   if (bf16 && q_t) { FP8BS_WL2(true, true) }
   else if (bf16) { FP8BS_WL2(true, false) }
@@ -812,6 +823,7 @@ extern "C" fp8bs_status fp8_quant_w_128x128(const void* w, int32_t w_dtype, int6
   else { FP8BS_WL2(false, false) }
 #undef FP8BS_WL2
 #undef FP8BS_WL
+#undef FP8BS_WLP
   return check_launch(fn);
 }
 
@@ -841,11 +853,13 @@ extern "C" fp8bs_status fp8_quant_act_dual(const void* x, int32_t x_dtype, int64
   constexpr int kT = FP8BS_DUAL_THREADS;
   const bool cached = 2 * rows * cols <= int64_t(FP8BS_CACHED_CODE_BYTES);
   begin_launch();
-#define FP8BS_DL(B, NT) hipLaunchKernelGGL((quant_dual_kernel<B, kT, true, NT>), grid, dim3(kT), 0, stream, x, ld_x, \
-                                           rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
+#define FP8BS_DLP(B, NT, P) hipLaunchKernelGGL((quant_dual_kernel<B, kT, true, NT, P>), grid, dim3(kT), 0, stream, \
+                                               x, ld_x, rows, cols, q, ld_q, scale, q_t, ld_qt, scale_t)
+#define FP8BS_DL(B, NT) do { if (per_wg > 1) FP8BS_DLP(B, NT, true); else FP8BS_DLP(B, NT, false); } while (0)
   if (x_dtype == FP8BS_BF16) { if (cached) FP8BS_DL(true, false); else FP8BS_DL(true, true); }
   else { if (cached) FP8BS_DL(false, false); else FP8BS_DL(false, true); }
 #undef FP8BS_DL
+#undef FP8BS_DLP
   return check_launch(fn);
 }
 
