@@ -236,6 +236,15 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
 // Output element types of the GEMM.
 enum OutKind : int { kOutF32 = 0, kOutBf16 = 1, kOutE4M3 = 2 };
 
+// 16 bytes from LDS to global memory with a nontemporal store.  The GEMM's
+// output is written once and not read again by the kernel; streaming it
+// keeps it from displacing the operand tiles that the XCD's L2 is serving
+// to the other workgroups.
+__device__ __forceinline__ void store16_nt(uint8_t* dst, const uint8_t* src) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst));
+}
+
 // Makes x live in registers here: values feeding it must be computed first.
 __device__ __forceinline__ void keep_in_vgprs(v16f& x) { asm volatile("" : "+v"(x)); }
 
@@ -745,9 +754,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
     for (int c = threadIdx.x; c < C::BM * 8; c += C::kThreads) {
       const int rl = c >> 3, ch = c & 7;
       const int64_t row = tile.row0 + rl;
-      if (row < tile.row_end)
-        *reinterpret_cast<uint4*>(yq + row * args.ldy + tile.n0 + 16 * ch) =
-            *reinterpret_cast<const uint4*>(ct + rl * kPitch + 16 * ch);
+      if (row < tile.row_end) store16_nt(yq + row * args.ldy + tile.n0 + 16 * ch, ct + rl * kPitch + 16 * ch);
     }
   } else {
     // Epilogue through LDS.  A lane's accumulators hold four consecutive
@@ -760,7 +767,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
     // takes the whole tile in one round; f32 output one wave column (TN
     // columns) per round.  Every tile of this configuration is one wave of
     // workgroups on the chip, so these stores are not hidden behind other
-    // tiles' matrix work: whole-line writes keep them short.
+    // tiles' matrix work: whole-line (and nontemporal) writes keep them
+    // short.
     constexpr int kElt = kOut == kOutBf16 ? 2 : 4;
     constexpr int kRounds = kOut == kOutBf16 ? 1 : C::WN;
     constexpr int kCols = C::BN / kRounds;            // columns per round
@@ -806,8 +814,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
         const int64_t row = tile.row0 + rl;
         const int64_t col = col0 + ch * (16 / kElt);
         if (row < tile.row_end && col < args.N)
-          *reinterpret_cast<uint4*>(ybase + (row * args.ldy + col) * kElt) =
-              *reinterpret_cast<const uint4*>((rl < kHalf ? lo_half : hi_half) + (rl % kHalf) * kPitch + ch * 16);
+          store16_nt(ybase + (row * args.ldy + col) * kElt, (rl < kHalf ? lo_half : hi_half) + (rl % kHalf) * kPitch + ch * 16);
       }
       if (rd + 1 < kRounds) __syncthreads();   // the next round rewrites the buffers
     }
