@@ -140,3 +140,23 @@ def test_delayed_scaling_every_bf16_value_stale_scale(fmt, stale):
     assert_scales_equal(a, np.float32([want_a]), "amax")
     assert_codes_equal(q, want_q, "codes")
     assert_scales_equal(host(hd), want_h, "history")
+
+
+@pytest.mark.parametrize("mode", ["current", "delayed"])
+def test_per_tensor_full_workload2_x_several_passes(mode):
+    """X [4096, 7168] is 3.67M chunks of 8: more than one pass of the kernels'
+    grid-stride loop (at most 512 workgroups x 4096 chunks per pass)."""
+    bits = inputs(2)["X"]
+    banner(f"per-tensor {mode} on the whole X {bits.shape}")
+    if mode == "current":
+        q, s, a = _run(dev_bf16(bits))
+        want_q, want_s, want_a = oracle.quant_tensor_current(f32(bits))
+    else:
+        hist = np.float32([30.0, 4.0, 0.0, 12.5])
+        hd = dev_f32(hist)
+        q, s, a = _run(dev_bf16(bits), history=hd)
+        want_q, want_s, want_a, want_h = oracle.quant_tensor_delayed(f32(bits), hist)
+        assert_scales_equal(host(hd), want_h, "history")
+    assert_scales_equal(a, np.float32([want_a]), "amax")
+    assert_scales_equal(s, np.float32([want_s]), "scale")
+    assert_codes_equal(q, want_q, "codes")
