@@ -66,7 +66,8 @@ def quant_tensor_delayed(x, history, fmt="e4m3", margin=0.0):
     history = np.asarray(history, dtype=np.float32)
     s = tensor_scale(history.max(), fmt, margin)
     _, enc = FORMATS[fmt]
-    codes = enc(x / s)                      # the encoder saturates at the format maximum
+    with np.errstate(over="ignore"):        # a stale scale may overflow x / s to inf,
+        codes = enc(x / s)                  # which the encoder saturates to the format maximum
     amax = np.float32(np.abs(x).max()) if x.size else np.float32(0.0)
     new_history = np.concatenate([[amax], history[:-1]]).astype(np.float32)
     return codes, s, amax, new_history
