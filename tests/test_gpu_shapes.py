@@ -120,26 +120,32 @@ def test_grouped_random_shape(counts, n, k, out):
 
 def _quant_cases():
     rng = np.random.default_rng(5)
-    return [(int(rng.integers(1, 600)), 128 * int(rng.integers(1, 12)), int(rng.integers(0, 3)) * 64)
-            for _ in range(10)]
+    return [(int(rng.integers(1, 600)), 128 * int(rng.integers(1, 12)), int(rng.integers(0, 3)) * 64,
+             "f32" if i % 3 == 2 else "bf16") for i in range(12)]
 
 
-@pytest.mark.parametrize("rows,cols,pad", _quant_cases())
-def test_quantizers_random_shape(rows, cols, pad):
+@pytest.mark.parametrize("rows,cols,pad,dtype", _quant_cases())
+def test_quantizers_random_shape(rows, cols, pad, dtype):
     """1x128 on any row count; 128x128, its transposed copy, 128x1T and the
     dual call on the 128-row prefix; codes and scales bit-exact, pitches from
-    sub-views."""
+    sub-views, bf16 and float32 inputs."""
     rng = np.random.default_rng([33, rows, cols, pad])
     x = (rng.standard_normal((rows, cols)) * np.exp2(rng.uniform(-8, 8, size=(rows, 1)))).astype(np.float32)
     x[rng.random((rows, cols)) < 2e-3] *= 300
-    bits = synth.f32_to_bf16_bits(x)
-    banner(f"quantizers random {rows}x{cols} pad {pad}")
-    full = torch.zeros((rows, cols + pad), dtype=torch.bfloat16, device="cuda")
-    full[:, :cols] = dev_bf16(bits)
+    banner(f"quantizers random {rows}x{cols} pad {pad} {dtype}")
+    if dtype == "bf16":
+        bits = synth.f32_to_bf16_bits(x)
+        xv = f32(bits)
+        full = torch.zeros((rows, cols + pad), dtype=torch.bfloat16, device="cuda")
+        full[:, :cols] = dev_bf16(bits)
+    else:
+        xv = x
+        full = torch.zeros((rows, cols + pad), dtype=torch.float32, device="cuda")
+        full[:, :cols] = torch.from_numpy(x).cuda()
     xd = full[:, :cols]
     q, s = fb.fp8_quant_act_1x128(xd)
     torch.cuda.synchronize()
-    want_q, want_s = oracle.quant_1x128(f32(bits))
+    want_q, want_s = oracle.quant_1x128(xv)
     assert_scales_equal(host(s), want_s, "1x128 scales")
     assert_codes_equal(host(q), want_q, "1x128 codes")
     r128 = rows - rows % 128
@@ -150,12 +156,12 @@ def test_quantizers_random_shape(rows, cols, pad):
     tq, ts = fb.fp8_quant_act_1x128(xb, "128x1_T")
     dq, ds, dqt, dst = fb.fp8_quant_act_dual(xb)
     torch.cuda.synchronize()
-    want_wq, want_ws = oracle.quant_128x128(f32(bits[:r128]))
+    want_wq, want_ws = oracle.quant_128x128(xv[:r128])
     assert_scales_equal(host(ws), want_ws, "128x128 scales")
     assert_codes_equal(host(wq), want_wq, "128x128 codes")
     assert_codes_equal(host(wqt), want_wq.T, "128x128 transposed codes")
     assert_scales_equal(host(wst), want_ws.T, "128x128 transposed scales")
-    want_tq, want_ts = oracle.quant_128x1_t(f32(bits[:r128]))
+    want_tq, want_ts = oracle.quant_128x1_t(xv[:r128])
     assert_codes_equal(host(tq), want_tq, "128x1T codes")
     assert_scales_equal(host(ts), want_ts, "128x1T scales")
     assert_codes_equal(host(dqt), want_tq, "dual transposed codes")
