@@ -1,14 +1,26 @@
 /* A plain C caller of the library on the GPU, with HIP memory and a HIP
- * stream of its own (no PyTorch): the linear step, i.e. one fp8_quant_batch
- * launch for X (1x128 tiles) and W (128x128 blocks), then
- * fp8_blockscaled_gemm with float32 output.
+ * stream of its own (no PyTorch).  Inputs and outputs go through files of
+ * raw little-endian values; out_prefix.<name> receives each output.
  *
- *   native_step M N K x.bin w.bin out_prefix
+ *   native_step step M N K x.bin w.bin out_prefix
+ *     The linear step: one fp8_quant_batch launch for X [M, K] (1x128 tiles)
+ *     and W [N, K] (128x128 blocks), then fp8_blockscaled_gemm into float32.
+ *     Writes .qa (M*K codes), .sa (M*K/128 float32), .qb (N*K codes), .sb
+ *     (N/128*K/128 float32) and .y (M*N float32).
  *
- * x.bin holds M*K bf16 bit patterns (uint16, row-major), w.bin N*K.  Writes
- * out_prefix.qa (M*K codes), .sa (M*K/128 float32), .qb (N*K codes), .sb
- * (N/128*K/128 float32) and .y (M*N float32).  Exit status 0 on success; a
- * library or HIP error is printed with the library's message. */
+ *   native_step moe G N K off.bin x.bin w.bin out_prefix
+ *     The grouped step: off.bin holds G+1 int32 row offsets (off[G] = M),
+ *     X [M, K] is quantized 1x128 by fp8_quant_act_1x128, the G expert
+ *     weights [G*N, K] by one fp8_quant_w_128x128 call, then
+ *     fp8_blockscaled_grouped_gemm into float32.  Same outputs as "step".
+ *
+ *   native_step dual R C x.bin out_prefix
+ *     fp8_quant_act_dual on X [R, C]: .q (R*C codes), .s (R*C/128 float32),
+ *     .qt (C*R codes of the transposed tiling), .st (C*R/128 float32).
+ *
+ * x.bin and w.bin hold bf16 bit patterns (uint16, row-major).  Exit status 0
+ * on success, 1 on a library or HIP error (printed with the library's
+ * message), 2 on bad usage or unreadable inputs. */
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -47,45 +59,56 @@ static void* read_file(const char* path, size_t bytes) {
   return p;
 }
 
-static int write_file(const char* prefix, const char* ext, const void* data, size_t bytes) {
+/* Copies `bytes` of device memory to out_prefix.ext. */
+static int save(const char* prefix, const char* ext, const void* dev, size_t bytes) {
+  void* host = malloc(bytes ? bytes : 1);
+  if (!host) return 1;
+  if (hipMemcpy(host, dev, bytes, hipMemcpyDeviceToHost) != hipSuccess) {
+    free(host);
+    return 1;
+  }
   char path[4096];
   snprintf(path, sizeof path, "%s.%s", prefix, ext);
   FILE* f = fopen(path, "wb");
-  if (!f) return 1;
-  size_t n = fwrite(data, 1, bytes, f);
-  fclose(f);
+  size_t n = f ? fwrite(host, 1, bytes, f) : 0;
+  if (f) fclose(f);
+  free(host);
   return n != bytes;
 }
 
-int main(int argc, char** argv) {
-  if (argc != 7) {
-    fprintf(stderr, "usage: %s M N K x.bin w.bin out_prefix\n", argv[0]);
-    return 2;
+/* A device buffer holding `bytes` of the file at `path` (NULL if unreadable). */
+static void* upload(const char* path, size_t bytes) {
+  void* host = read_file(path, bytes);
+  if (!host) return NULL;
+  void* dev = NULL;
+  if (hipMalloc(&dev, bytes ? bytes : 1) != hipSuccess ||
+      hipMemcpy(dev, host, bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(dev);
+    dev = NULL;
   }
-  const int64_t M = atoll(argv[1]), N = atoll(argv[2]), K = atoll(argv[3]);
+  free(host);
+  return dev;
+}
+
+static int run_step(int64_t M, int64_t N, int64_t K, const char* xf, const char* wf, const char* pre) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 128 || N % 128) {
     fprintf(stderr, "need M, N, K > 0 with N and K multiples of 128\n");
     return 2;
   }
   const size_t nx = (size_t)(M * K), nw = (size_t)(N * K), ny = (size_t)(M * N);
   const size_t nsa = (size_t)(M * (K / 128)), nsb = (size_t)((N / 128) * (K / 128));
-  uint16_t* hx = (uint16_t*)read_file(argv[4], nx * 2);
-  uint16_t* hw = (uint16_t*)read_file(argv[5], nw * 2);
-  if (!hx || !hw) {
+  void* dx = upload(xf, nx * 2);
+  void* dw = upload(wf, nw * 2);
+  if (!dx || !dw) {
     fprintf(stderr, "cannot read the inputs\n");
     return 2;
   }
-
-  void *dx, *dw, *dqa, *dsa, *dqb, *dsb, *dy;
-  HIP_OK(hipMalloc(&dx, nx * 2));
-  HIP_OK(hipMalloc(&dw, nw * 2));
+  void *dqa, *dsa, *dqb, *dsb, *dy;
   HIP_OK(hipMalloc(&dqa, nx));
   HIP_OK(hipMalloc(&dsa, nsa * 4));
   HIP_OK(hipMalloc(&dqb, nw));
   HIP_OK(hipMalloc(&dsb, nsb * 4));
   HIP_OK(hipMalloc(&dy, ny * 4));
-  HIP_OK(hipMemcpy(dx, hx, nx * 2, hipMemcpyHostToDevice));
-  HIP_OK(hipMemcpy(dw, hw, nw * 2, hipMemcpyHostToDevice));
   hipStream_t stream;
   HIP_OK(hipStreamCreate(&stream));
 
@@ -102,32 +125,117 @@ int main(int argc, char** argv) {
                                         (const float*)dsb, FP8BS_BSCALE_BLOCK128, dy, FP8BS_F32, N, stream));
   HIP_OK(hipStreamSynchronize(stream));
 
-  size_t most = ny * 4;
-  if (nx > most) most = nx;
-  if (nw > most) most = nw;
-  if (nsa * 4 > most) most = nsa * 4;
-  if (nsb * 4 > most) most = nsb * 4;
-  void* out = malloc(most);
-  if (!out) return 1;
-  int bad = 0;
-  HIP_OK(hipMemcpy(out, dqa, nx, hipMemcpyDeviceToHost));
-  bad |= write_file(argv[6], "qa", out, nx);
-  HIP_OK(hipMemcpy(out, dsa, nsa * 4, hipMemcpyDeviceToHost));
-  bad |= write_file(argv[6], "sa", out, nsa * 4);
-  HIP_OK(hipMemcpy(out, dqb, nw, hipMemcpyDeviceToHost));
-  bad |= write_file(argv[6], "qb", out, nw);
-  HIP_OK(hipMemcpy(out, dsb, nsb * 4, hipMemcpyDeviceToHost));
-  bad |= write_file(argv[6], "sb", out, nsb * 4);
-  HIP_OK(hipMemcpy(out, dy, ny * 4, hipMemcpyDeviceToHost));
-  bad |= write_file(argv[6], "y", out, ny * 4);
-  if (bad) {
+  if (save(pre, "qa", dqa, nx) || save(pre, "sa", dsa, nsa * 4) || save(pre, "qb", dqb, nw) ||
+      save(pre, "sb", dsb, nsb * 4) || save(pre, "y", dy, ny * 4)) {
     fprintf(stderr, "cannot write the outputs\n");
     return 1;
   }
   HIP_OK(hipStreamDestroy(stream));
   HIP_OK(hipFree(dx)); HIP_OK(hipFree(dw)); HIP_OK(hipFree(dqa)); HIP_OK(hipFree(dsa));
   HIP_OK(hipFree(dqb)); HIP_OK(hipFree(dsb)); HIP_OK(hipFree(dy));
-  free(out); free(hx); free(hw);
   printf("native step %lld x %lld x %lld ok\n", (long long)M, (long long)N, (long long)K);
   return 0;
+}
+
+static int run_moe(int32_t G, int64_t N, int64_t K, const char* of, const char* xf, const char* wf,
+                   const char* pre) {
+  if (G < 1 || N <= 0 || K <= 0 || K % 128 || N % 128) {
+    fprintf(stderr, "need G >= 1, N, K > 0 with N and K multiples of 128\n");
+    return 2;
+  }
+  int32_t* off = (int32_t*)read_file(of, (size_t)(G + 1) * 4);
+  if (!off) {
+    fprintf(stderr, "cannot read the offsets\n");
+    return 2;
+  }
+  const int64_t M = off[G];
+  if (M <= 0) {
+    fprintf(stderr, "need at least one row\n");
+    return 2;
+  }
+  const size_t nx = (size_t)(M * K), nw = (size_t)(G * N * K), ny = (size_t)(M * N);
+  const size_t nsa = (size_t)(M * (K / 128)), nsb = (size_t)(G * (N / 128) * (K / 128));
+  void* dx = upload(xf, nx * 2);
+  void* dw = upload(wf, nw * 2);
+  void* doff = upload(of, (size_t)(G + 1) * 4);
+  if (!dx || !dw || !doff) {
+    fprintf(stderr, "cannot read the inputs\n");
+    return 2;
+  }
+  void *dqa, *dsa, *dqb, *dsb, *dy;
+  HIP_OK(hipMalloc(&dqa, nx));
+  HIP_OK(hipMalloc(&dsa, nsa * 4));
+  HIP_OK(hipMalloc(&dqb, nw));
+  HIP_OK(hipMalloc(&dsb, nsb * 4));
+  HIP_OK(hipMalloc(&dy, ny * 4));
+  hipStream_t stream;
+  HIP_OK(hipStreamCreate(&stream));
+  FP8BS_OK_OR_FAIL(fp8_quant_act_1x128(dx, FP8BS_BF16, M, K, K, FP8BS_TILE_1x128, (uint8_t*)dqa, K, (float*)dsa,
+                                       stream));
+  /* The G weights stacked as one [G*N, K] matrix: its 128x128 blocks are the
+     experts' blocks, in the [G, N/128, K/128] scale layout. */
+  FP8BS_OK_OR_FAIL(fp8_quant_w_128x128(dw, FP8BS_BF16, G * N, K, K, (uint8_t*)dqb, K, (float*)dsb, NULL, 0,
+                                       stream));
+  FP8BS_OK_OR_FAIL(fp8_blockscaled_grouped_gemm(M, N, K, G, (const int32_t*)doff, (const uint8_t*)dqa,
+                                                (const float*)dsa, (const uint8_t*)dqb, (const float*)dsb, dy,
+                                                FP8BS_F32, stream));
+  HIP_OK(hipStreamSynchronize(stream));
+
+  if (save(pre, "qa", dqa, nx) || save(pre, "sa", dsa, nsa * 4) || save(pre, "qb", dqb, nw) ||
+      save(pre, "sb", dsb, nsb * 4) || save(pre, "y", dy, ny * 4)) {
+    fprintf(stderr, "cannot write the outputs\n");
+    return 1;
+  }
+  HIP_OK(hipStreamDestroy(stream));
+  HIP_OK(hipFree(dx)); HIP_OK(hipFree(dw)); HIP_OK(hipFree(doff)); HIP_OK(hipFree(dqa)); HIP_OK(hipFree(dsa));
+  HIP_OK(hipFree(dqb)); HIP_OK(hipFree(dsb)); HIP_OK(hipFree(dy));
+  free(off);
+  printf("native moe %d experts, %lld rows, N %lld, K %lld ok\n", (int)G, (long long)M, (long long)N, (long long)K);
+  return 0;
+}
+
+static int run_dual(int64_t R, int64_t C, const char* xf, const char* pre) {
+  if (R <= 0 || C <= 0 || R % 128 || C % 128) {
+    fprintf(stderr, "need R, C > 0, multiples of 128\n");
+    return 2;
+  }
+  const size_t n = (size_t)(R * C), ns = n / 128;
+  void* dx = upload(xf, n * 2);
+  if (!dx) {
+    fprintf(stderr, "cannot read the input\n");
+    return 2;
+  }
+  void *dq, *ds, *dqt, *dst;
+  HIP_OK(hipMalloc(&dq, n));
+  HIP_OK(hipMalloc(&ds, ns * 4));
+  HIP_OK(hipMalloc(&dqt, n));
+  HIP_OK(hipMalloc(&dst, ns * 4));
+  hipStream_t stream;
+  HIP_OK(hipStreamCreate(&stream));
+  FP8BS_OK_OR_FAIL(fp8_quant_act_dual(dx, FP8BS_BF16, R, C, C, (uint8_t*)dq, C, (float*)ds, (uint8_t*)dqt, R,
+                                      (float*)dst, stream));
+  HIP_OK(hipStreamSynchronize(stream));
+  if (save(pre, "q", dq, n) || save(pre, "s", ds, ns * 4) || save(pre, "qt", dqt, n) || save(pre, "st", dst, ns * 4)) {
+    fprintf(stderr, "cannot write the outputs\n");
+    return 1;
+  }
+  HIP_OK(hipStreamDestroy(stream));
+  HIP_OK(hipFree(dx)); HIP_OK(hipFree(dq)); HIP_OK(hipFree(ds)); HIP_OK(hipFree(dqt)); HIP_OK(hipFree(dst));
+  printf("native dual %lld x %lld ok\n", (long long)R, (long long)C);
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  if (argc == 8 && strcmp(argv[1], "step") == 0)
+    return run_step(atoll(argv[2]), atoll(argv[3]), atoll(argv[4]), argv[5], argv[6], argv[7]);
+  if (argc == 9 && strcmp(argv[1], "moe") == 0)
+    return run_moe((int32_t)atoi(argv[2]), atoll(argv[3]), atoll(argv[4]), argv[5], argv[6], argv[7], argv[8]);
+  if (argc == 6 && strcmp(argv[1], "dual") == 0)
+    return run_dual(atoll(argv[2]), atoll(argv[3]), argv[4], argv[5]);
+  fprintf(stderr,
+          "usage: %s step M N K x.bin w.bin out_prefix\n"
+          "       %s moe G N K off.bin x.bin w.bin out_prefix\n"
+          "       %s dual R C x.bin out_prefix\n",
+          argv[0], argv[0], argv[0]);
+  return 2;
 }

@@ -1,9 +1,10 @@
 """The library from a plain C program on the GPU, with no PyTorch in the
 process: tests/native_step.c allocates HIP memory, creates its own stream,
-quantizes X per 1x128 tile and W per 128x128 block in one batched launch,
-runs the block-scaled GEMM into float32 and writes every output to files.
-Codes and scales must equal the oracle's bit for bit, Y must lie within the
-GEMM tolerance."""
+calls the entry points and writes every output to files.  Codes and scales
+must equal the oracle's bit for bit, GEMM outputs must lie within the GEMM
+tolerance.  Modes: the linear step (batched 1x128 + 128x128 quantization,
+dense GEMM), the grouped step (1x128 quantization, the experts' weights in
+one 128x128 call, grouped GEMM) and the dual-orientation quantizer."""
 import os
 import subprocess
 
@@ -34,23 +35,33 @@ def exe():
     return EXE
 
 
-def _run(exe, tmp_path, x_bits, w_bits):
+def _write(path, arr, dtype):
+    np.ascontiguousarray(arr, dtype=dtype).tofile(path)
+    return str(path)
+
+
+def _run(args, what):
+    banner(f"native C {what}")
+    r = subprocess.run([str(a) for a in args], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def _read(pre, ext, dtype, shape):
+    return np.fromfile(f"{pre}.{ext}", dtype=dtype).reshape(shape)
+
+
+def _run_step(exe, tmp_path, x_bits, w_bits):
     m, k = x_bits.shape
     n = w_bits.shape[0]
-    xf, wf, pre = tmp_path / "x.bin", tmp_path / "w.bin", tmp_path / "out"
-    np.ascontiguousarray(x_bits, dtype=np.uint16).tofile(xf)
-    np.ascontiguousarray(w_bits, dtype=np.uint16).tofile(wf)
-    banner(f"native C step {m}x{n}x{k}")
-    r = subprocess.run([exe, str(m), str(n), str(k), str(xf), str(wf), str(pre)],
-                       capture_output=True, text=True, timeout=120)
-    assert r.returncode == 0, r.stdout + r.stderr
-    rd = lambda ext, dt, shape: np.fromfile(f"{pre}.{ext}", dtype=dt).reshape(shape)
-    return (rd("qa", np.uint8, (m, k)), rd("sa", np.float32, (m, k // 128)),
-            rd("qb", np.uint8, (n, k)), rd("sb", np.float32, (n // 128, k // 128)),
-            rd("y", np.float32, (m, n)))
+    pre = tmp_path / "out"
+    _run([exe, "step", m, n, k, _write(tmp_path / "x.bin", x_bits, np.uint16),
+          _write(tmp_path / "w.bin", w_bits, np.uint16), pre], f"step {m}x{n}x{k}")
+    return (_read(pre, "qa", np.uint8, (m, k)), _read(pre, "sa", np.float32, (m, k // 128)),
+            _read(pre, "qb", np.uint8, (n, k)), _read(pre, "sb", np.float32, (n // 128, k // 128)),
+            _read(pre, "y", np.float32, (m, n)))
 
 
-def _check(x_bits, w_bits, outs, rows=None):
+def _check_step(x_bits, w_bits, outs, rows=None):
     qa, sa, qb, sb, y = outs
     want_qa, want_sa = oracle.quant_1x128(f32(x_bits))
     want_qb, want_sb = oracle.quant_128x128(f32(w_bits))
@@ -69,7 +80,7 @@ def test_native_c_step_ragged(exe, tmp_path):
     rng = np.random.default_rng([41, 300])
     x = synth.normal_bf16(rng, (300, 1024), 1.0, 0.005, 50.0)
     w = synth.normal_bf16(rng, (256, 1024), 0.02)
-    _check(x, w, _run(exe, tmp_path, x, w))
+    _check_step(x, w, _run_step(exe, tmp_path, x, w))
 
 
 def test_native_c_step_workload_4096x2048x7168(exe, tmp_path):
@@ -77,5 +88,48 @@ def test_native_c_step_workload_4096x2048x7168(exe, tmp_path):
     seeded sample of rows that holds the first and the last."""
     s = synth.SHAPES[2]
     inp = synth.workload_inputs(2)
-    outs = _run(exe, tmp_path, inp["X"], inp["W"])
-    _check(inp["X"], inp["W"], outs, synth.sample_rows(s["M"], 256, seed=41, must=(0, s["M"] - 1)))
+    outs = _run_step(exe, tmp_path, inp["X"], inp["W"])
+    _check_step(inp["X"], inp["W"], outs, synth.sample_rows(s["M"], 256, seed=41, must=(0, s["M"] - 1)))
+
+
+def test_native_c_grouped(exe, tmp_path):
+    """Five experts, one empty and none a multiple of 128 rows (300 rows in
+    all), N = 256, K = 768; every output checked."""
+    counts = np.array([70, 0, 129, 1, 100])
+    off = synth.offsets_from_counts(counts)
+    g, n, k, m = len(counts), 256, 768, int(off[-1])
+    rng = np.random.default_rng([42, m])
+    x = synth.normal_bf16(rng, (m, k), 1.0, 0.001, 100.0)
+    w = synth.normal_bf16(rng, (g * n, k), 0.02)
+    pre = tmp_path / "out"
+    _run([exe, "moe", g, n, k, _write(tmp_path / "off.bin", off, np.int32),
+          _write(tmp_path / "x.bin", x, np.uint16), _write(tmp_path / "w.bin", w, np.uint16), pre],
+         f"grouped counts {counts.tolist()} N {n} K {k}")
+    qa, sa = _read(pre, "qa", np.uint8, (m, k)), _read(pre, "sa", np.float32, (m, k // 128))
+    qb, sb = _read(pre, "qb", np.uint8, (g * n, k)), _read(pre, "sb", np.float32, (g * n // 128, k // 128))
+    y = _read(pre, "y", np.float32, (m, n))
+    want_qa, want_sa = oracle.quant_1x128(f32(x))
+    want_qb, want_sb = oracle.quant_128x128(f32(w))
+    assert_scales_equal(sa, want_sa, "X 1x128 scales")
+    assert_codes_equal(qa, want_qa, "X 1x128 codes")
+    assert_scales_equal(sb, want_sb, "experts' 128x128 scales")
+    assert_codes_equal(qb, want_qb, "experts' 128x128 codes")
+    ref, bound = oracle.grouped_gemm_ref(off, want_qa, want_sa, want_qb.reshape(g, n, k),
+                                         want_sb.reshape(g, n // 128, k // 128))
+    ok = oracle.gemm_tolerance_ok(y.astype(np.float64), ref, bound, "f32")
+    assert ok.all(), f"{(~ok).sum()} of {ok.size} outside tolerance"
+
+
+def test_native_c_dual(exe, tmp_path):
+    """Both activation tilings of X [384, 640] from one call."""
+    r, c = 384, 640
+    rng = np.random.default_rng([43, r, c])
+    x = synth.normal_bf16(rng, (r, c), 1.0, 0.005, 50.0)
+    pre = tmp_path / "out"
+    _run([exe, "dual", r, c, _write(tmp_path / "x.bin", x, np.uint16), pre], f"dual {r}x{c}")
+    want_q, want_s = oracle.quant_1x128(f32(x))
+    want_qt, want_st = oracle.quant_128x1_t(f32(x))
+    assert_codes_equal(_read(pre, "q", np.uint8, (r, c)), want_q, "1x128 codes")
+    assert_scales_equal(_read(pre, "s", np.float32, (r, c // 128)), want_s, "1x128 scales")
+    assert_codes_equal(_read(pre, "qt", np.uint8, (c, r)), want_qt, "128x1 transposed codes")
+    assert_scales_equal(_read(pre, "st", np.float32, (c, r // 128)), want_st, "128x1 transposed scales")
