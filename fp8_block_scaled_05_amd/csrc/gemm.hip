@@ -151,13 +151,16 @@ struct alignas(16) Stage {
   uint8_t b[BN * 128];
 };
 
-// Scales of four consecutive K blocks: [row][kb % 4].  A 64-lane load fills
-// 16 rows x 4 blocks (16 cache lines), where loading one block per step would
-// touch one line per row.  Two of these alternate.
+// Scales of four consecutive K blocks.  A scales: [row][kb % 4]; a 64-lane
+// load fills 16 rows x 4 blocks (16 cache lines), where loading one block
+// per step would touch one line per row.  Per-row B scales: [column / 16]
+// [kb % 4][column % 16], so that the four consecutive columns a lane needs
+// for one K block are 16 contiguous bytes (one LDS read); the same 64-lane
+// load fills one such [4][16] piece.  Two groups alternate.
 template <int BM, int BN, bool kRowScale>
 struct alignas(16) ScaleGroup {
   float sa[BM][4];
-  float sb[kRowScale ? BN : 1][4];
+  float sb[kRowScale ? BN / 16 : 1][4][kRowScale ? 16 : 1];
 };
 
 // 16-byte chunk swizzle of a 128-byte LDS row.
@@ -317,12 +320,15 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
     rs_b[v] = make_rsrc(tile.bmat + (tile.n0 + r) * args.ldb, uint64_t(max(cols - r, int64_t(0))) * args.ldb);
   }
   // Scale-group loads: load u of this wave covers rows 16 (u * NW + wave) +
-  // lane / 4 and K block 4 g + lane % 4, again with a descriptor per u that
-  // starts at its row group.  The group's K blocks go in the VGPR offset: a
-  // lane whose K block is past the last one reads the next row's first
-  // scales (unused) or, on the last row, zero.
+  // lane / 4 and K block 4 g + lane % 4 of the A scales (B scale columns
+  // 16 (u * NW + wave) + lane % 16 and K block 4 g + lane / 16, in the
+  // layout of ScaleGroup), again with a descriptor per u that starts at its
+  // row group.  The group's K blocks go in the VGPR offset: a lane whose K
+  // block is past the last one reads the next row's first scales (unused)
+  // or, on the last row, zero.
   constexpr int SUA = C::kScaleLoadsA, SUB = kRowScale ? C::kScaleLoadsB : 1;
   const int voff_s = ((16 * wave + (lane >> 2)) * KB + (lane & 3)) * 4;
+  const int voff_sb = ((16 * wave + (lane & 15)) * KB + (lane >> 4)) * 4;
   i32x4 rs_sa[SUA], rs_sb[SUB];
 #pragma unroll
   for (int u = 0; u < SUA; ++u) {
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
     if constexpr (kRowScale) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
-        dma4(rs_sb[u], lds_addr(&d.sb[16 * (u * NW + wave)][0]), vo, 0);
+        dma4(rs_sb[u], lds_addr(&d.sb[u * NW + wave][0][0]), voff_sb + g * 16, 0);
     }
   };
 
@@ -390,9 +396,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
   // fixed per unrolled step (see the main loops).  Otherwise (FP8 path,
   // per-row B scales) p[0] holds every block and is promoted at the end of
   // its step.  (Deferring per-row promotions the same way measured no
-  // faster: that path is bound by its vector instructions, the conversions
-  // plus a scale product per accumulator, not by their placement.)  Either
-  // way each accumulator receives the same FMAs in the same order.
+  // faster.)  Either way each accumulator receives the same FMAs in the same
+  // order.
   constexpr bool kLag = kWiden && !kRowScale;
   v16f p[2][SM][SN];
   float cl[SM];   // kLag: sa * sb of the pending block
@@ -409,18 +414,16 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][j][r] = __builtin_fmaf(p[par][i][j][r], c, acc[i][j][r]);
   };
-  // Per-row B scales: column slab j of block kbv from p[par], with A scales
-  // ca.  The slab's 16 accumulators per lane are 16 columns, each with its
-  // own B scale (read from the scale group) and product sa * sb.
-  auto promote_row = [&](auto par_c, int j, int kbv, const float (&ca)[SM]) {
+  // Per-row B scales: column slab j of a block from p[par], with A scales
+  // ca and B scales sbr.  The slab's 16 accumulators per lane are 16
+  // columns, each with its own B scale and product sa * sb.
+  auto promote_row = [&](auto par_c, int j, const float (&ca)[SM], const float (&sbr)[SN][16]) {
     constexpr int par = decltype(par_c)::value;
-    const Sg& g = sg[(kbv >> 2) & 1];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float sbn = g.sb[wn * C::TN + 32 * j + 8 * (r >> 2) + 4 * hk + (r & 3)][kbv & 3];
 #pragma unroll
       for (int i = 0; i < SM; ++i)
-        acc[i][j][r] = __builtin_fmaf(p[par][i][j][r], ca[i] * sbn, acc[i][j][r]);
+        acc[i][j][r] = __builtin_fmaf(p[par][i][j][r], ca[i] * sbr[j][r], acc[i][j][r]);
     }
   };
   // kLag: the pending block's subtiles s = i * SN + j with s / 2 == q.  The
@@ -522,6 +525,25 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
     constexpr bool kIn = kLag && decltype(in_c)::value;
     constexpr bool kKeep = kLag && decltype(keep_c)::value;
     const Sg& scl = sg[(kb >> 2) & 1];
+    // Per-row B scales of the lane's 16 columns per slab, read before the
+    // matrix work so that their latency is hidden by it (four 16-byte reads
+    // per slab; reading them one by one at the promotion made the weight-
+    // gradient GEMM 5-6% slower).  The scale group is visible from the start
+    // of the step on.
+    float sbr[SN][16];
+    if constexpr (kRowScale) {
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const int c = wn * C::TN + 32 * j + 8 * rq + 4 * hk;
+          const float4 v4 = *reinterpret_cast<const float4*>(&scl.sb[c >> 4][kb & 3][c & 15]);
+          sbr[j][4 * rq] = v4.x;
+          sbr[j][4 * rq + 1] = v4.y;
+          sbr[j][4 * rq + 2] = v4.z;
+          sbr[j][4 * rq + 3] = v4.w;
+        }
+    }
     // The scheduling fences keep the compiler from hoisting later slices'
     // reads and widening ahead of the current slice's matrix work, which
     // would raise register pressure past the two-waves-per-SIMD budget.
@@ -578,7 +600,7 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_kernel(const GemmArgs arg
       // the slab's B scales across it and spill.
 #pragma unroll
       for (int j = 0; j < SN; ++j) {
-        promote_row(Par{}, j, kb, ca);
+        promote_row(Par{}, j, ca, sbr);
 #pragma unroll
         for (int i = 0; i < SM; ++i) keep_in_vgprs(acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);

@@ -76,32 +76,65 @@ def test_old_scheme_reads_past_the_last_row():
     assert max(addr for _, addr in acc) + 16 > rows * ld
 
 
-def scale_accesses(rows, kb_count, nw, loads):
-    """(row, K block, byte offset from the tile's first scale) of every
-    4-byte scale load that passes the range check."""
+def lane_row_kb(lane, layout):
+    """(row within the wave's 16, K block within the group of 4) that a lane
+    loads: A scales lane / 4 and lane % 4; per-row B scales lane % 16 and
+    lane / 16 (gemm.hip: voff_s and voff_sb)."""
+    if layout == "a":
+        return lane >> 2, lane & 3
+    return lane & 15, lane >> 4
+
+
+def scale_accesses(rows, kb_count, nw, loads, layout="a"):
+    """(row, K block, byte offset from the tile's first scale, LDS float
+    index in the scale group) of every 4-byte scale load that passes the
+    range check.  Each wave's load u lands in 64 consecutive floats of the
+    group, lane by lane."""
     out = []
     groups = (kb_count + 3) // 4
     for u, wave, lane, g in itertools.product(range(loads), range(nw), range(64), range(groups)):
         base = 16 * u * nw * kb_count * 4
         records = max(rows - 16 * u * nw, 0) * kb_count * 4
-        voff = ((16 * wave + (lane >> 2)) * kb_count + (lane & 3)) * 4 + g * 16
+        r, k = lane_row_kb(lane, layout)
+        voff = ((16 * wave + r) * kb_count + k) * 4 + g * 16
         if voff >= records:
             continue
-        out.append((16 * u * nw + 16 * wave + (lane >> 2), 4 * g + (lane & 3), base + voff))
+        out.append((16 * u * nw + 16 * wave + r, 4 * g + k, base + voff, 64 * (u * nw + wave) + lane))
     return out
+
+
+def lds_index(row, kb, layout):
+    """Where the kernel reads the scale of (row, K block) in its group: A
+    scales [row][kb % 4]; per-row B scales [row / 16][kb % 4][row % 16]."""
+    if layout == "a":
+        return 4 * row + (kb & 3)
+    return 64 * (row >> 4) + 16 * (kb & 3) + (row & 15)
 
 
 @pytest.mark.parametrize("cfg", sorted(CONFIGS))
 @pytest.mark.parametrize("kb_count", [1, 2, 5, 56])
-def test_scale_loads_stay_inside_existing_rows(cfg, kb_count):
+@pytest.mark.parametrize("layout", ["a", "b_row"])
+def test_scale_loads_stay_inside_existing_rows(cfg, kb_count, layout):
     bm, bn, nw = CONFIGS[cfg]
-    for tile_rows in (bm, bn):
+    for tile_rows in ((bm, bn) if layout == "a" else (bn,)):
         loads = tile_rows // 16 // nw
         for rows in sorted({1, 3, 15, 16, 17, 100, tile_rows - 1, tile_rows}):
             needed = set()
-            for row, kb, addr in scale_accesses(rows, kb_count, nw, loads):
+            for row, kb, addr, lds in scale_accesses(rows, kb_count, nw, loads, layout):
                 assert 0 <= addr and addr + 4 <= rows * kb_count * 4, (row, kb, addr)
                 if kb < kb_count:                  # a real scale: it is where it belongs
                     assert row < rows and addr == (row * kb_count + kb) * 4
+                    # and the kernel reads it from the LDS slot it landed in
+                    assert lds == lds_index(row, kb, layout), (row, kb, lds)
                     needed.add((row, kb))
             assert len(needed) == rows * kb_count
+
+
+def test_b_row_scale_reads_are_aligned_quads():
+    """The per-row B scales a lane needs for one K block and slab (columns
+    c .. c + 3, c = 64 wn + 32 j + 8 rq + 4 hk) are one aligned 16-byte run
+    of the scale group."""
+    for wn, j, rq, hk, kb in itertools.product(range(2), range(2), range(4), range(2), range(4)):
+        c = 64 * wn + 32 * j + 8 * rq + 4 * hk
+        idx = [lds_index(c + t, kb, "b_row") for t in range(4)]
+        assert idx == list(range(idx[0], idx[0] + 4)) and idx[0] % 4 == 0
