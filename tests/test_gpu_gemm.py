@@ -340,6 +340,22 @@ def test_gemm_repeat_bitwise_identical():
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+@pytest.mark.parametrize("m,n,k", [(1000, 528, 1024), (4096, 2048, 1024)])
+def test_gemm_row_scales_repeat_bitwise_identical(m, n, k):
+    """Per-row B scales on the 128x128 tile (ragged M and N) and on the
+    256x128 tile: repeated calls give the same bits."""
+    banner(f"gemm repeatability, per-row B scales {m}x{n}x{k}")
+    g = torch.Generator(device="cuda").manual_seed(m + n)
+    x = torch.randn((m, k), device="cuda", generator=g).to(torch.bfloat16)
+    w = (torch.randn((n, k), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    a, sa = fb.fp8_quant_act_1x128(x)
+    b, sb = fb.fp8_quant_act_1x128(w)
+    ys = [fb.fp8_blockscaled_gemm(a, sa, b, sb, b_kind="row", out_dtype=torch.float32) for _ in range(3)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int32), y.view(torch.int32))
+
+
 def test_gemm_zero_m_is_noop():
     banner("gemm M=0")
     a = torch.empty((0, 256), dtype=torch.uint8, device="cuda")
