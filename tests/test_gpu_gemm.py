@@ -143,12 +143,12 @@ def test_wgrad_workload5():
     dyt, sdyt = fb.fp8_quant_act_1x128(dev_bf16(d["dY"]), "128x1_T")  # [2048, 8192]
     y = fb.fp8_blockscaled_gemm(xt, sxt, dyt, sdyt, "row", torch.float32)
     torch.cuda.synchronize()
+    # sampled rows of dW, every column (each column has its own B scales)
     rows = synth.sample_rows(xt.shape[0], 128, seed=55, must=[0, xt.shape[0] - 1])
-    cols = synth.sample_rows(dyt.shape[0], 256, seed=56, must=[0, dyt.shape[0] - 1])
     ah, sah = oracle.quant_128x1_t(f32(d["X"][:, rows]))
-    bh, sbh = oracle.quant_128x1_t(f32(d["dY"][:, cols]))
+    bh, sbh = oracle.quant_128x1_t(f32(d["dY"]))
     ref, bound = oracle.blockscaled_gemm_ref(ah, sah, bh, sbh, "row")
-    _check_tol(_y_host(y)[rows][:, cols], ref, bound, "f32", "wgrad")
+    _check_tol(_y_host(y)[rows], ref, bound, "f32", "wgrad")
 
 
 # ---------------------------------------------------------------- exact cases
