@@ -12,8 +12,9 @@
 // once with 16-byte loads, every code written once with 8- or 16-byte
 // stores.  Each 128-element tile's amax is reduced across the lanes that hold
 // it (a 16-lane DPP row for 1x128), the scale and its reciprocal are formed
-// once per tile, and x/s is evaluated with a 3-instruction exact quotient for
-// bf16 inputs (IEEE division for f32 inputs).
+// once per tile (without a division sequence for bf16 inputs), and x/s is
+// evaluated with a 3-instruction exact quotient for bf16 inputs (IEEE
+// division for f32 inputs).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -51,6 +52,40 @@ template <bool kBf16>
 __device__ __forceinline__ float quotient(float x, float s, float r) {
   if constexpr (kBf16) return div_bf16_by_scale(x, s, r);
   else return x / s;
+}
+
+// The scale s = fl32(amax / 448) (with the guard) and r, close to 1 / s, of
+// a tile whose amax is a bf16 value, without IEEE division sequences:
+//  - amax / 448 = (amax / 7) / 64.  The quotient by 7 is Markstein's
+//    correction of amax * fl32(1/7), which returns fl32(amax / 7) for every
+//    bf16 amax whose scale passes the guard (checked against exact rational
+//    arithmetic for all of them; every smaller amax still gives a value at
+//    or below the guard), and the division by 64 is exact there.
+//  - r is the hardware reciprocal refined by one Newton-Raphson step.  It
+//    only feeds the quotient correction of div_bf16_by_scale, whose result
+//    is checked against fl32(x / s) for every pair of bf16 values x and
+//    amax.
+__device__ __forceinline__ void scale_recip_bf16(float amax, float& s, float& r) {
+  constexpr float kInv7 = 0x1.24924ap-3f;   // fl32(1/7)
+  const float q0 = amax * kInv7;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-q0, 7.0f, amax), kInv7, q0);
+  const float sc = q1 * 0x1p-6f;
+  s = sc > kScaleGuard ? sc : 1.0f;
+  const float r0 = __builtin_amdgcn_rcpf(s);
+  r = __builtin_fmaf(__builtin_fmaf(-s, r0, 1.0f), r0, r0);
+}
+
+// Scale and reciprocal of a tile: the division-free form above for bf16
+// inputs, IEEE division for float32 inputs (whose quotient is an IEEE
+// division too, so r is not used there).
+template <bool kBf16>
+__device__ __forceinline__ void tile_scale_recip(float amax, float& s, float& r) {
+  if constexpr (kBf16) {
+    scale_recip_bf16(amax, s, r);
+  } else {
+    s = tile_scale(amax);
+    r = 1.0f / s;
+  }
 }
 
 template <bool kBf16>
@@ -124,9 +159,8 @@ __global__ __launch_bounds__(256) void quant_1x128_kernel(const void* __restrict
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const float amax = row16_max(absmax8(v[u]));
-    const float s = tile_scale(amax);
-    const float r = 1.0f / s;
+    float s, r;
+    tile_scale_recip<kBf16>(row16_max(absmax8(v[u])), s, r);
     const uint2 codes = encode8<kBf16>(v[u], s, r);
     if (tile[u] < n_tiles) {
       uint8_t* dst = q + int64_t(row[u]) * ld_q + int64_t(kb[u]) * 128 + sub * 8;
@@ -221,8 +255,8 @@ __global__ __launch_bounds__(256) void quant_128x1_t_kernel(const void* __restri
   for (int h = 0; h < 2; ++h) {
     const int64_t col = c0 + 2 * cp + h;
     const float* val = h ? b : a;
-    const float s = tile_scale(h ? m1 : m0);
-    const float r = 1.0f / s;
+    float s, r;
+    tile_scale_recip<kBf16>(h ? m1 : m0, s, r);
     float qv[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) qv[i] = quotient<kBf16>(val[i], s, r);
@@ -365,8 +399,8 @@ __global__ __launch_bounds__(kThreads) void quant_128x128_kernel(const void* __r
     m = red[0];
 #pragma unroll
     for (int i = 1; i < kWaves; ++i) m = fmaxf(m, red[i]);
-    const float s = tile_scale(m);
-    const float r = 1.0f / s;
+    float s, r;
+    tile_scale_recip<kBf16>(m, s, r);
 
 #pragma unroll
     for (int p = 0; p < kRows; ++p) {
@@ -478,8 +512,8 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
     if constexpr (kRowOut) {
 #pragma unroll
       for (int p = 0; p < kRows; ++p) {
-        const float s = tile_scale(row16_max(absmax8(v[p])));
-        const float r = 1.0f / s;
+        float s, r;
+        tile_scale_recip<kBf16>(row16_max(absmax8(v[p])), s, r);
         const int64_t row = r0 + rbase + kRowStep * p;
         store_codes8<kNT>(q + row * ld_q + c0 + cc, encode8<kBf16>(v[p], s, r));
         if ((t & 15) == 0) store_scale(&scale[row * row_kb + bj], s);
@@ -506,9 +540,10 @@ __global__ __launch_bounds__(kThreads) void quant_dual_kernel(const void* __rest
       float m = cmax[0][t];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) m = fmaxf(m, cmax[w][t]);
-      const float s = tile_scale(m);
+      float s, r;
+      tile_scale_recip<kBf16>(m, s, r);
       csc[0][t] = s;
-      csc[1][t] = 1.0f / s;
+      csc[1][t] = r;
       store_scale(&scale_t[(c0 + t) * col_kb + bi], s);
     }
     __syncthreads();
@@ -626,8 +661,8 @@ __device__ __forceinline__ void act_tiles(const BatchJob& jb, uint32_t wave) {
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
-    const float s = tile_scale(row16_max(absmax8(v[u])));
-    const float r = 1.0f / s;
+    float s, r;
+    tile_scale_recip<kBf16>(row16_max(absmax8(v[u])), s, r);
     const uint2 codes = encode8<kBf16>(v[u], s, r);
     if (tile[u] < n_tiles) {
       store_codes8(jb.q + int64_t(row[u]) * jb.ld_q + int64_t(kb[u]) * 128 + sub * 8, codes);
@@ -661,8 +696,8 @@ __device__ __forceinline__ void w_block(const BatchJob& jb, uint32_t blk, float*
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float s = tile_scale(m);
-  const float r = 1.0f / s;
+  float s, r;
+  tile_scale_recip<kBf16>(m, s, r);
 #pragma unroll
   for (int p = 0; p < kRows; ++p) {
     float v[8];
