@@ -209,24 +209,55 @@ __device__ __forceinline__ bool locate_tile(const GemmArgs& args, Tile& tile) {
   tile.n0 = int64_t(tn) * C::BN;
   if constexpr (kGrouped) {
     // Find the group holding virtual M tile `tm`.  Offsets are clamped into
-    // [0, M], and each group starts no earlier than the previous one ends
-    // (a group whose end lies before that is empty), so the groups' row
-    // ranges never overlap whatever the table holds; for a valid table this
-    // changes nothing.
-    int vm = tm, g = 0;
-    int64_t lo = 0, hi = 0, prev_hi = 0;
-    bool found = false;
-    for (; g < args.G; ++g) {
-      lo = max(prev_hi, min(int64_t(args.off[g]), int64_t(args.M)));
-      hi = max(lo, min(int64_t(args.off[g + 1]), int64_t(args.M)));
-      prev_hi = hi;
-      const int cnt = int((hi - lo + C::BM - 1) / C::BM);
-      if (vm < cnt) { found = true; break; }
-      vm -= cnt;
+    // [0, M], and each group starts no earlier than the previous one ends (a
+    // group whose end lies before that is empty), so the groups' row ranges
+    // never overlap whatever the table holds; for a valid table this changes
+    // nothing.  With c_g the clamped offsets and P_g = max(0, c_0 .. c_g),
+    // group g owns rows [P_g, P_g+1).  Every wave searches 64 groups per
+    // step, one per lane: a prefix maximum of c gives the ranges, a prefix
+    // sum of their tile counts the first group whose tiles reach past `tm`.
+    // (A search one group at a time took 1.99 ms instead of 1.58 ms for a
+    // GEMM of 256 experts, and 7.7 ms instead of 2.5 ms for 1024.)
+    const int lane = threadIdx.x & 63;
+    int vm = tm;          // tiles still to skip
+    int run = 0;          // P at the start of this step
+    int gsel = -1, lo_s = 0, hi_s = 0, vm_s = 0;
+    for (int g0 = 0; g0 < args.G && gsel < 0; g0 += 64) {
+      const int g = g0 + lane;
+      const bool real = g < args.G;
+      const int cg = real ? min(max(args.off[g], 0), args.M) : 0;
+      const int cn = real ? min(max(args.off[g + 1], 0), args.M) : 0;
+      int pm = cg;        // max(c_g0 .. c_g)
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(pm, d);
+        if (lane >= d) pm = max(pm, t);
+      }
+      const int lo_g = max(run, pm);
+      const int hi_g = max(lo_g, cn);
+      const int cnt = real ? (hi_g - lo_g + C::BM - 1) / C::BM : 0;
+      int ps = cnt;       // tiles of groups g0 .. g
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(ps, d);
+        if (lane >= d) ps += t;
+      }
+      const uint64_t hit = __ballot(vm < ps);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        gsel = g0 + l;
+        lo_s = __shfl(lo_g, l);
+        hi_s = __shfl(hi_g, l);
+        vm_s = vm - (__shfl(ps, l) - __shfl(cnt, l));
+      } else {
+        vm -= __shfl(ps, 63);
+        run = __shfl(hi_g, 63);
+      }
     }
-    if (!found) return false;
-    tile.row0 = lo + int64_t(vm) * C::BM;
-    tile.row_end = hi;
+    const int g = __builtin_amdgcn_readfirstlane(gsel);
+    if (g < 0) return false;
+    tile.row0 = int64_t(__builtin_amdgcn_readfirstlane(lo_s)) + int64_t(__builtin_amdgcn_readfirstlane(vm_s)) * C::BM;
+    tile.row_end = __builtin_amdgcn_readfirstlane(hi_s);
     tile.bmat += int64_t(g) * args.b_group_stride;
     tile.bscale += int64_t(g) * args.bs_group_stride;
   } else {

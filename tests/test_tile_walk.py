@@ -8,7 +8,10 @@ and locate_tile), checked without a GPU.
 - Grouped: for any offset table, valid or not, the clamped group ranges are
   disjoint and inside [0, M], the launch's upper bound ceil(M / BM) + G on
   the M tiles is never exceeded, and every row of every group lies in
-  exactly one tile of that group.
+  exactly one tile of that group.  The kernel finds a tile's group with a
+  64-lane search (prefix maximum of the clamped offsets, prefix sum of the
+  tile counts); its model returns the same group and rows as the one-group-
+  at-a-time rule for every tile, also with more than 64 groups.
 """
 import numpy as np
 import pytest
@@ -132,3 +135,49 @@ def test_walk_without_the_remainder_term_is_caught():
         in_g = w - g * per_group
         seen.add((g * GROUP_M + in_g % gm, in_g // gm))
     assert len(seen) < n_wg
+
+
+def wave_locate(tm, off, m, bm):
+    """The kernel's search, 64 groups per step (lane l takes group g0 + l):
+    (group, first row, end row) of virtual M tile tm, or None."""
+    g_count = len(off) - 1
+    vm, run = tm, 0
+    for g0 in range(0, g_count, 64):
+        real = [g0 + l < g_count for l in range(64)]
+        cg = [min(max(off[g0 + l], 0), m) if real[l] else 0 for l in range(64)]
+        cn = [min(max(off[g0 + l + 1], 0), m) if real[l] else 0 for l in range(64)]
+        pm = list(np.maximum.accumulate(cg))
+        lo = [max(run, p) for p in pm]
+        hi = [max(lo[l], cn[l]) for l in range(64)]
+        cnt = [(hi[l] - lo[l] + bm - 1) // bm if real[l] else 0 for l in range(64)]
+        ps = list(np.cumsum(cnt))
+        hits = [l for l in range(64) if vm < ps[l]]
+        if hits:
+            l = hits[0]
+            return g0 + l, lo[l] + (vm - (ps[l] - cnt[l])) * bm, hi[l]
+        vm -= ps[63]
+        run = hi[63]
+    return None
+
+
+def _many_group_tables():
+    rng = np.random.default_rng(21)
+    out = []
+    for _ in range(12):
+        g = int(rng.integers(60, 300))
+        m = int(rng.integers(1, 20000))
+        if rng.random() < 0.5:
+            cuts = np.sort(rng.integers(0, m + 1, size=g - 1))
+            out.append(([0, *cuts.tolist(), m], m))
+        else:
+            out.append((rng.integers(-50, m + 50, size=g + 1).tolist(), m))
+    return out
+
+
+@pytest.mark.parametrize("bm", [128, 256])
+@pytest.mark.parametrize("off,m", _tables() + _many_group_tables())
+def test_wave_search_matches_the_sequential_rule(off, m, bm):
+    ranges = group_tiles(off, m, bm)
+    tiles_m = (m + bm - 1) // bm + len(off) - 1
+    for tm in range(tiles_m):
+        assert wave_locate(tm, off, m, bm) == locate(tm, ranges, bm), tm
