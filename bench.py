@@ -49,8 +49,8 @@ METRIC = "FP8 block-scaled GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)
 # `bench.py --calib-copy` (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the same counter reads for the device copy of known size that --calib-copy
 # adds; valid only for the GEMM source it was measured on (sha256 of gemm.hip).
-TRAFFIC = {"gemm_sha256": "f64eb8a01ce62f6b18f3f6c3962b790457fc3d49717a13da8d096eb4d7716c27",
-           "bytes_per_launch": 137177086,   # 120.40 MB read (FETCH_SIZE x 1.99944) + 16.78 MB written
+TRAFFIC = {"gemm_sha256": "20995fa41966ad92536126e9c5510da124f793cbc723c4f80e386083acfa9ee0",
+           "bytes_per_launch": 137175349,   # 120.40 MB read (FETCH_SIZE x 1.99944) + 16.78 MB written
            "source": "profiles/bench_linear_4096x2048x7168_counters.md"}
 CALIB_COPY_BYTES = 128 << 20
 
