@@ -330,6 +330,59 @@ def test_grouped_bad_offsets_deterministic(off, ranges):
     assert np.all(y[~written] == -3.0)
 
 
+def _clamped_ranges(off, m):
+    """The header's rule for any table: group g owns rows [P_g, P_g+1) with
+    P_g the largest offset among off[0..g] clamped into [0, m]."""
+    c = np.clip(np.asarray(off, np.int64), 0, m)
+    p = np.maximum.accumulate(c)
+    return {g: (int(p[g]), int(p[g + 1])) for g in range(len(off) - 1) if p[g + 1] > p[g]}
+
+
+@pytest.mark.parametrize("kind", ["valid", "bad"])
+def test_grouped_many_groups(kind):
+    """More groups than one wave's 64-lane expert search covers: 150 groups
+    of random sizes (a third of them empty), and an increasing table of 140
+    groups with a fifth of its offsets scrambled (decreasing, negative, past
+    M); every group's rows against the oracle, rows of no group keep their
+    canary."""
+    rng = np.random.default_rng(26 if kind == "valid" else 27)
+    n, k = 128, 256
+    if kind == "valid":
+        counts = rng.integers(0, 12, size=150)
+        counts[rng.random(150) < 0.33] = 0
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+        m = int(off[-1])
+    else:                    # an increasing table with a fifth of its entries broken
+        m = 1400
+        off = np.sort(rng.integers(0, m + 1, size=141))
+        bad = np.nonzero(rng.random(141) < 0.2)[0]
+        neg = rng.random(len(bad)) < 0.5
+        off[bad[neg]] = -rng.integers(1, 40, size=int(neg.sum()))            # negative
+        off[bad[~neg]] -= rng.integers(1, 30, size=int((~neg).sum()))        # below the previous one
+        off[130] = m + 37                                                     # past M: the rest is empty
+        off = off.astype(np.int32)
+    g = len(off) - 1
+    ranges = _clamped_ranges(off, m)
+    a = rng.integers(0, 0x30, size=(m, k), dtype=np.uint8)
+    sa = (rng.random((m, 2)) + 0.5).astype(np.float32)
+    b = rng.integers(0, 0x30, size=(g, n, k), dtype=np.uint8)
+    sb = (rng.random((g, 1, 2)) + 0.5).astype(np.float32)
+    ybuf = torch.full((m + 2, n), -3.0, dtype=torch.float32, device="cuda")
+    banner(f"grouped with {g} groups ({kind} table), M {m}")
+    fb.fp8_blockscaled_grouped_gemm(_dev(off), _dev(a), _dev(sa), _dev(b), _dev(sb), y=ybuf[1:m + 1])
+    torch.cuda.synchronize()
+    yb = host(ybuf)
+    assert np.all(yb[0] == -3.0) and np.all(yb[-1] == -3.0)
+    y = yb[1:m + 1]
+    written = np.zeros(m, bool)
+    assert len(ranges) > 64
+    for grp, (lo, hi) in ranges.items():
+        ref, bound = oracle.blockscaled_gemm_ref(a[lo:hi], sa[lo:hi], b[grp], sb[grp])
+        _check_tol(y[lo:hi], ref, bound, "f32", f"group {grp} rows {lo}..{hi}")
+        written[lo:hi] = True
+    assert np.all(y[~written] == -3.0)
+
+
 def test_gemm_repeat_bitwise_identical():
     d = inputs(1)
     banner("gemm repeatability")
