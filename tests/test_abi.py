@@ -230,6 +230,35 @@ def test_last_error_is_per_call_text(L):
     assert "200" in fb.last_error()
 
 
+def test_last_error_is_per_thread(L):
+    """The error text is thread-local: a failing call on another thread
+    between a call and its fp8bs_last_error() does not replace its text."""
+    import threading
+    bar = threading.Barrier(2, timeout=30)
+    out = {}
+
+    def first():
+        out["a_status"] = _gemm(L, K=100, lda=112, ldb=112)
+        bar.wait()          # the other thread now fails with its own text
+        bar.wait()
+        out["a"] = fb.last_error()
+
+    def second():
+        bar.wait()
+        out["b_status"] = _w(L, rows=200)
+        out["b"] = fb.last_error()
+        bar.wait()
+
+    ts = [threading.Thread(target=first), threading.Thread(target=second)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join(60)
+    assert out["a_status"] == SHAPE and out["b_status"] == SHAPE
+    assert "K=100" in out["a"] and "200" not in out["a"]
+    assert "200" in out["b"] and "K=100" not in out["b"]
+
+
 def test_binding_raises_typed_error():
     with pytest.raises(fb.Fp8bsError) as e:
         fb._check(2)
