@@ -37,8 +37,9 @@
  *  - Alignment: every code/input/output pointer 16-byte aligned and every
  *    row pitch a multiple of 16 bytes; scale pointers 4-byte aligned.
  *  - Quantization rounds to nearest (ties to even) and saturates at +-448; it
- *    never reports a range error.  Inputs must be finite (NaN/Inf inputs
- *    give unspecified codes).
+ *    never reports a range error.  Inputs must be finite: a NaN or infinity
+ *    gives unspecified codes and scale for the tiles that hold it, and
+ *    leaves every other tile as it would be without it.
  *  - Tiled dimensions must be whole multiples of 128 (FP8BS_ERR_SHAPE);
  *    partial tail tiles are rejected, not dropped.
  *  - Thread-safe: the only global state is the thread-local error text.
