@@ -145,6 +145,9 @@ def extra_cpu_baselines(shrink=1):
     K; fewer rows), quantized by the oracle and multiplied by its float64
     per-128-K-block reference, so every figure includes quantization.
     Throughput is 2 * rows * cols * K of the sample over its wall time.
+    Every stage is timed on its own; the full workload's oracle time is
+    estimated by scaling each quantization stage by the full tensor's
+    element count and each GEMM stage by the full GEMM's flops.
     `shrink` divides every row count (the tests use a small sample)."""
     import numpy as np
     import oracle
@@ -153,55 +156,72 @@ def extra_cpu_baselines(shrink=1):
     nthreads = blas_threads()
     res = {}
 
-    def timed(name, flops, sample, fn):
-        t0 = time.perf_counter()
-        fn()
-        dt = time.perf_counter() - t0
-        res[name] = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
-                     "sample": sample, "seconds": round(dt, 3),
-                     "cores": {"quantize": 1, "gemm": int(nthreads)}}
+    def timed(name, flops, sample, stages):
+        """stages: (stage name, cores, fn, factor from the sample to the full workload)."""
+        per, total, full = {}, 0.0, 0.0
+        for sname, cores, fn, factor in stages:
+            t0 = time.perf_counter()
+            fn()
+            dt = time.perf_counter() - t0
+            per[sname] = {"seconds": round(dt, 3), "cores": int(cores), "to_full": round(factor, 3)}
+            total += dt
+            full += dt * factor
+        res[name] = {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+                     "sample": sample, "seconds": round(total, 3),
+                     "full_workload_seconds_est": round(full, 1),
+                     "cores": {"quantize": 1, "gemm": int(nthreads)}, "stages": per}
 
     k = 7168
     r1, r2, r4 = 1024 // shrink, 2048 // shrink, 4096 // shrink
-    # Dense FFN: 1024 rows of X, 2048 rows (16 row blocks) of the block-spread W.
+    d = {}
+    # Dense FFN [8192, 18432, 7168]: 1024 rows of X, 2048 rows (16 row
+    # blocks) of the block-spread W.
     x = f32(synth.normal_bf16(synth.rng_for(3, synth.X_ID), (r1, k), 1.0, 0.001, 100.0))
     w = f32(synth.block_spread_bf16(synth.rng_for(3, synth.W_ID), (r2, k), 0.02))
-
-    def ffn():
-        a, sa = oracle.quant_1x128(x)
-        b, sb = oracle.quant_128x128(w)
-        oracle.blockscaled_gemm_ref(a, sa, b, sb)
     timed("ffn_8192x18432x7168", 2.0 * r1 * r2 * k,
-          f"X[{r1},7168] 1x128 + W[{r2},7168] 128x128 (block spread) + GEMM {r1}x{r2}x7168", ffn)
+          f"X[{r1},7168] 1x128 + W[{r2},7168] 128x128 (block spread) + GEMM {r1}x{r2}x7168", [
+              ("quant_x_1x128", 1, lambda: d.update(a=oracle.quant_1x128(x)), 8192 / r1),
+              ("quant_w_128x128", 1, lambda: d.update(b=oracle.quant_128x128(w)), 18432 / r2),
+              ("gemm", nthreads, lambda: oracle.blockscaled_gemm_ref(*d["a"], *d["b"]),
+               8192 * 18432 / (r1 * r2)),
+          ])
 
-    # MoE: one expert's full weight [4096, 7168] and 512 of its tokens.
+    # MoE [32768 tokens, 16 experts of 4096 x 7168]: one expert's full
+    # weight and 512 of its tokens.
     x = f32(synth.normal_bf16(synth.rng_for(4, synth.X_ID), (r1 // 2, k), 1.0, 0.001, 100.0))
     w = f32(synth.weight(4, r4, k, expert=0))
-
-    def moe():
-        a, sa = oracle.quant_1x128(x)
-        b, sb = oracle.quant_128x128(w)
-        oracle.grouped_gemm_ref(np.array([0, r1 // 2], np.int32), a, sa, b[None], sb[None])
+    off = np.array([0, r1 // 2], np.int32)
     timed("moe_grouped_32768x4096x7168_g16", 2.0 * (r1 // 2) * r4 * k,
-          f"one expert: X[{r1 // 2},7168] 1x128 + W[{r4},7168] 128x128 + grouped GEMM {r1 // 2}x{r4}x7168", moe)
+          f"one expert: X[{r1 // 2},7168] 1x128 + W[{r4},7168] 128x128 + grouped GEMM {r1 // 2}x{r4}x7168", [
+              ("quant_x_1x128", 1, lambda: d.update(a=oracle.quant_1x128(x)), 32768 / (r1 // 2)),
+              ("quant_w_128x128", 1, lambda: d.update(b=oracle.quant_128x128(w)), 16 * 4096 / r4),
+              ("grouped_gemm", nthreads,
+               lambda: oracle.grouped_gemm_ref(off, *d["a"], d["b"][0][None], d["b"][1][None]),
+               32768 * 4096 / ((r1 // 2) * r4)),
+          ])
 
-    # Backward: 1024 tokens.  dgrad dY[1024,2048] x W[2048,7168] (W quantized
-    # 128x128, used transposed); wgrad X^T dY with both operands 128x1 along
-    # the tokens.
+    # Backward [8192 tokens]: 1024 tokens.  dgrad dY[1024,2048] x W[2048,7168]
+    # (W quantized 128x128, used transposed); wgrad X^T dY with both
+    # operands 128x1 along the tokens.
     t, h, f = r1, 7168, 2048
     dy = f32(synth.normal_bf16(synth.rng_for(5, synth.DY_ID), (t, f), 1e-3))
     x = f32(synth.normal_bf16(synth.rng_for(5, synth.X_ID), (t, h), 1.0, 0.001, 100.0))
     w = f32(synth.weight(5, f, h))
+    tok = 8192 / t
 
-    def backward():
-        g, sg = oracle.quant_1x128(dy)
-        b, sb = oracle.quant_128x128(w)
-        oracle.blockscaled_gemm_ref(g, sg, np.ascontiguousarray(b.T), np.ascontiguousarray(sb.T))
-        xt, sxt = oracle.quant_128x1_t(x)
-        gt, sgt = oracle.quant_128x1_t(dy)
-        oracle.blockscaled_gemm_ref(xt, sxt, gt, sgt, "row")
+    def dgrad():
+        b, sb = d["w"]
+        oracle.blockscaled_gemm_ref(*d["g"], np.ascontiguousarray(b.T), np.ascontiguousarray(sb.T))
+
     timed("backward_dgrad_wgrad", 2.0 * (t * h * f) * 2,
-          f"{t} tokens: dY 1x128 + W 128x128 + dgrad {t}x7168x2048; X and dY 128x1 + wgrad 7168x2048x{t}", backward)
+          f"{t} tokens: dY 1x128 + W 128x128 + dgrad {t}x7168x2048; X and dY 128x1 + wgrad 7168x2048x{t}", [
+              ("quant_dy_1x128", 1, lambda: d.update(g=oracle.quant_1x128(dy)), tok),
+              ("quant_w_128x128", 1, lambda: d.update(w=oracle.quant_128x128(w)), 1.0),
+              ("dgrad_gemm", nthreads, dgrad, tok),
+              ("quant_x_128x1_t", 1, lambda: d.update(xt=oracle.quant_128x1_t(x)), tok),
+              ("quant_dy_128x1_t", 1, lambda: d.update(gt=oracle.quant_128x1_t(dy)), tok),
+              ("wgrad_gemm", nthreads, lambda: oracle.blockscaled_gemm_ref(*d["xt"], *d["gt"], "row"), tok),
+          ])
     return res
 
 

@@ -75,4 +75,8 @@ def test_extra_oracle_samples_run():
         assert v["kind"] == "oracle" and v["unit"] == "TFLOP/s"
         assert v["value"] > 0 and v["seconds"] > 0 and v["sample"]
         assert v["cores"]["quantize"] == 1 and v["cores"]["gemm"] >= 1
+        # every stage timed, the estimate scales each one up to the full workload
+        assert abs(sum(st["seconds"] for st in v["stages"].values()) - v["seconds"]) < 0.01
+        assert all(st["to_full"] >= 1 for st in v["stages"].values())
+        assert v["full_workload_seconds_est"] >= v["seconds"]
     assert "X[128,7168]" in res["ffn_8192x18432x7168"]["sample"]
