@@ -608,7 +608,7 @@ constexpr int kMaxBatchJobs = 8;
 // 1x128 steps per wave.  At the lower occupancy of this kernel, four steps
 // keep more loads in flight than the single kernel's two: X [4096, 7168]
 // 1x128 + W [2048, 7168] 128x128 took 23.2 us with 3 or 4 steps, 23.8 us
-// with 2, 24.4 with 6 and 25.0 with 8 (alternated on one box).
+// with 2, 24.4 with 6 and 25.0 with 8 (alternated on one MI355X).
 #ifndef FP8BS_BATCH_U
 #define FP8BS_BATCH_U 4
 #endif
