@@ -79,6 +79,25 @@ def test_gemm_random_shape(m, n, k, kind, out, pad):
         assert np.isnan(tail).all(), "the row pitch's margin was written"
 
 
+@pytest.mark.parametrize("m,n,k,kind,out,pad", _gemm_cases()[::3])
+def test_gemm_random_shape_repeats_bitwise(m, n, k, kind, out, pad):
+    """Every third random shape again, twice on the same operands: the two
+    outputs are identical bit for bit (no order-dependent reduction or race
+    in any tile configuration)."""
+    rng = np.random.default_rng([34, m, n, k])
+    a = torch.from_numpy(_codes(rng, (m, k))).cuda()
+    b = torch.from_numpy(_codes(rng, (n, k))).cuda()
+    sa = torch.from_numpy(_scales(rng, (m, k // 128))).cuda()
+    sb = torch.from_numpy(_scales(rng, (n // 128 if kind == "block128" else n, k // 128))).cuda()
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    banner(f"gemm random repeat {m}x{n}x{k} {kind} {out}")
+    y1 = fb.fp8_blockscaled_gemm(a, sa, b, sb, kind, dt)
+    y2 = fb.fp8_blockscaled_gemm(a, sa, b, sb, kind, dt)
+    torch.cuda.synchronize()
+    iv = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(y1.view(iv), y2.view(iv))
+
+
 def _grouped_cases():
     rng = np.random.default_rng(77)
     cases = []
